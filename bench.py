@@ -1,0 +1,234 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+One step is one fa_fwd launch over the whole workload (inputs resident in
+HBM).  Default workload: the wide-logit run B=2, H=16, N=8192, d=128,
+non-causal (the throughput target).  Prints ONE JSON line with the metric,
+the roofline of the kernel (MFMA-bound, BF16 dense peak), the CPU oracle
+baseline, and per-run / per-variant timings.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense BF16 flop/clk/CU (the 2.5 PF spec)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fa_fwd_wide.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_107_amd", "csrc", "fa_fwd.hip"),
+                  os.path.join(ROOT, "exact_attention_107_amd", "build.py")]
+
+
+def kernel_fingerprint() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def to_dev(bits, torch):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def time_launches(launch, steps: int, warmup: int, torch):
+    """Warmup, then `steps` launches bracketed by synchronisation; per-launch
+    HIP events on the launch stream give the kernel's average duration."""
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record()
+        launch()
+        e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) for s, e in ev]
+    return wall * 1e3 / steps, float(np.mean(per)), float(np.median(per)), float(np.min(per))
+
+
+def cpu_baseline(inp, target_s: float):
+    """The oracle on a bounded row sample of the same workload, all host cores."""
+    import oracle
+    from exact_attention_107_amd.workloads import flops
+    threads = oracle.default_threads()
+    lengths = np.asarray(inp["lengths"])
+    B, H = len(lengths), inp["H"]
+    rng = np.random.Generator(np.random.PCG64(0))
+
+    def rows_of(count):
+        b = rng.integers(B, size=count)
+        n = lengths[b]
+        i = (rng.random(count) * n).astype(np.int64)
+        h = rng.integers(H, size=count)
+        return np.stack([b, h, i], axis=1).astype(np.int64)
+
+    def credited(rows):
+        # 4 * (visible keys) * d per row: the per-row share of 4 n^2 d (halved causal)
+        n = lengths[rows[:, 0]].astype(np.float64)
+        vis = (rows[:, 2] + 1).astype(np.float64) if inp["causal"] else n
+        return float(np.sum(4.0 * vis * inp["d"]))
+
+    calib = rows_of(max(threads * 4, 64))
+    t0 = time.perf_counter()
+    oracle.attention(inp["q"], inp["k"], inp["v"], scale=inp["scale"], causal=inp["causal"],
+                     cu_seqlens=inp["cu_seqlens"], rows=calib, nthreads=threads)
+    dt = time.perf_counter() - t0
+    count = int(min(max(len(calib) * target_s / max(dt, 1e-3), len(calib)), 2_000_000))
+    rows = rows_of(count)
+    t0 = time.perf_counter()
+    oracle.attention(inp["q"], inp["k"], inp["v"], scale=inp["scale"], causal=inp["causal"],
+                     cu_seqlens=inp["cu_seqlens"], rows=rows, nthreads=threads)
+    dt = time.perf_counter() - t0
+    f = credited(rows)
+    total = flops(lengths, H, inp["d"], inp["causal"])
+    return {
+        "value": f / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": f"{count} random query rows of the {inp['name']} run "
+                  f"({f / total * 100:.3f}% of its credited flops), fp64, {dt:.1f} s wall",
+        "seconds": dt, "full_run_seconds_extrapolated": dt * total / f,
+    }
+
+
+def traffic_for(fingerprint: str):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_fingerprint") != fingerprint:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="wide")
+    ap.add_argument("--extra", type=int, default=1, help="also time the other runs and variants")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the attention forward here is a single-GPU "
+              "kernel with no collectives; run it with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    from exact_attention_107_amd import fa
+    from exact_attention_107_amd.workloads import RUNS, flops, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    fa.load()
+    props = torch.cuda.get_device_properties(0)
+    run = RUNS[args.workload]
+    log(f"[bench] generating {run.name} inputs")
+    inp = make_inputs(run)
+    inp["name"] = run.name
+    q, k, v = (to_dev(inp[x], torch) for x in ("q", "k", "v"))
+    cu = torch.from_numpy(inp["cu_seqlens"]).cuda() if inp["cu_seqlens"] is not None else None
+    o = torch.empty_like(q)
+    lse_shape = (inp["H"], inp["T"]) if cu is not None else (inp["B"], inp["H"], inp["N"])
+    lse = torch.empty(lse_shape, dtype=torch.float32, device="cuda")
+    f = flops(inp["lengths"], inp["H"], inp["d"], inp["causal"])
+
+    def launch():
+        fa.fwd(q, k, v, causal=inp["causal"], scale=inp["scale"], cu_seqlens=cu, out=o, lse=lse)
+
+    log(f"[bench] timing {args.steps} steps after {args.warmup} warmup")
+    ms_step, ms_kernel, ms_med, ms_min = time_launches(launch, args.steps, args.warmup, torch)
+    value = f / (ms_step * 1e-3) / 1e12
+    achieved = f / (ms_kernel * 1e-3) / 1e12
+    log(f"[bench] {run.name}: {ms_step:.4f} ms/step, kernel {ms_kernel:.4f} ms, {achieved:.1f} TFLOP/s")
+
+    fp = kernel_fingerprint()
+    out = {
+        "metric": "attention fwd TFLOP/s (bf16, causal & non-causal) and % of MFMA BF16 peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {
+            "workload": f"{run.name}: B={inp['B']} H={inp['H']} N={inp['N']} d={inp['d']} "
+                        f"causal={inp['causal']} Q,K~N(0,{run.sigma_qk}^2) 1% K rows x8, V~N(0,1)",
+            "B": inp["B"], "H": inp["H"], "N": inp["N"], "d": inp["d"], "causal": inp["causal"],
+            "flops_per_step": f, "tile_rows": fa.tile_rows(inp["d"]), "tile_keys": fa.tile_keys(inp["d"]),
+        },
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_for(fp),
+            "kernel_ms_mean": round(ms_kernel, 5), "kernel_ms_median": round(ms_med, 5),
+            "kernel_ms_min": round(ms_min, 5),
+            "per_launch": "4*B*H*N^2*d flops (halved if causal) / mean HIP-event duration",
+        },
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "arch": getattr(props, "gcnArchName", "")},
+        "kernel_fingerprint": fp,
+    }
+
+    if args.extra:
+        runs = {}
+        for name in ("mid", "mid_causal", "long_causal", "varlen_causal", "wide_d64", "wide_d256"):
+            r = RUNS[name]
+            log(f"[bench] run {name}")
+            ri = make_inputs(r)
+            rq, rk, rv = (to_dev(ri[x], torch) for x in ("q", "k", "v"))
+            rcu = torch.from_numpy(ri["cu_seqlens"]).cuda() if ri["cu_seqlens"] is not None else None
+            ro = torch.empty_like(rq)
+            rl_shape = (ri["H"], ri["T"]) if rcu is not None else (ri["B"], ri["H"], ri["N"])
+            rl = torch.empty(rl_shape, dtype=torch.float32, device="cuda")
+            rf = flops(ri["lengths"], ri["H"], ri["d"], ri["causal"])
+
+            def rlaunch():
+                fa.fwd(rq, rk, rv, causal=ri["causal"], scale=ri["scale"], cu_seqlens=rcu, out=ro, lse=rl)
+
+            _, kms, _, _ = time_launches(rlaunch, 20, 3, torch)
+            runs[name] = {"ms": round(kms, 4), "tflops": round(rf / (kms * 1e-3) / 1e12, 1),
+                          "pct_of_peak": round(100 * rf / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 1)}
+            del rq, rk, rv, ro, rl
+        out["runs"] = runs
+        variants = {}
+        for em, en in ((fa.EXP_HW, "hw"), (fa.EXP_POLY, "poly"), (fa.EXP_MIXED, "mixed")):
+            for rm, rn in ((fa.RESCALE_ALWAYS, "always"), (fa.RESCALE_STRICT, "strict"),
+                           (fa.RESCALE_THRESHOLD, "threshold")):
+                def vlaunch():
+                    fa.fwd(q, k, v, causal=inp["causal"], scale=inp["scale"], out=o, lse=lse,
+                           exp_mode=em, rescale_mode=rm)
+                _, kms, _, _ = time_launches(vlaunch, 20, 3, torch)
+                variants[f"{en}/{rn}"] = {"ms": round(kms, 4),
+                                          "tflops": round(f / (kms * 1e-3) / 1e12, 1)}
+        out["variants"] = variants
+
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,147 @@
+"""Python binding of libfa.so: argument marshalling only.
+
+Every step of the attention forward runs in the library's HIP kernel; this
+module checks tensors, allocates the outputs with torch, passes raw device
+pointers and torch's current HIP stream, and turns error codes into
+exceptions.  If the library is not built, every call raises: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+# enum fa_exp_mode / fa_rescale_mode of include/fa.h
+EXP_HW, EXP_POLY, EXP_MIXED = 0, 1, 2
+RESCALE_ALWAYS, RESCALE_STRICT, RESCALE_THRESHOLD = 0, 1, 2
+EXPORTS = ("fa_fwd", "fa_fwd_variant", "fa_strerror", "fa_tile_rows", "fa_tile_keys")
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"fa error {code}: {msg}")
+        self.code = code
+
+
+def load(path: str | None = None):
+    """Load libfa.so and declare its C signatures (raises if not built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(p)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    common = [vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_float, i32, vp, vp]
+    lib.fa_fwd.argtypes = common
+    lib.fa_fwd.restype = i32
+    lib.fa_fwd_variant.argtypes = common + [i32, i32]
+    lib.fa_fwd_variant.restype = i32
+    lib.fa_strerror.argtypes = [i32]
+    lib.fa_strerror.restype = ctypes.c_char_p
+    lib.fa_tile_rows.argtypes = [i32]
+    lib.fa_tile_rows.restype = i32
+    lib.fa_tile_keys.argtypes = [i32]
+    lib.fa_tile_keys.restype = i32
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return load().fa_strerror(int(code)).decode()
+
+
+def _check(t: torch.Tensor, name: str, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+        scale: float | None = None, cu_seqlens: torch.Tensor | None = None,
+        exp_mode: int | None = None, rescale_mode: int | None = None,
+        out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+        stream: torch.cuda.Stream | None = None):
+    """Exact attention forward on the GPU.
+
+    q, k, v     bf16, ``[B, N, H, d]`` (dense) or ``[T, H, d]`` with
+                ``cu_seqlens`` (int32, ``[B+1]``, on the same device).
+    scale       defaults to ``1/sqrt(d)``, rounded to fp32.
+    exp_mode, rescale_mode   None for the library default (``fa_fwd``), else
+                one of the EXP_* / RESCALE_* constants (``fa_fwd_variant``).
+    out, lse    optional preallocated outputs (``o`` like q; ``lse`` fp32
+                ``[B, H, N]`` or ``[H, T]``).
+    Returns ``(o, lse)``.  The kernel is queued on ``stream`` (default: the
+    current stream); nothing is synchronised.
+    """
+    lib = load()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a GPU tensor")
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, name, torch.bfloat16, dev)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must have the same shape")
+    if cu_seqlens is None:
+        if q.dim() != 4:
+            raise ValueError("dense q must be [B, N, H, d]")
+        B, N, H, d = q.shape
+        lse_shape = (B, H, N)
+        cu_ptr = None
+    else:
+        _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        if q.dim() != 3 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("packed q must be [T, H, d] with cu_seqlens [B+1]")
+        N, H, d = q.shape
+        B = cu_seqlens.numel() - 1
+        lse_shape = (H, N)
+        cu_ptr = cu_seqlens.data_ptr()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", torch.bfloat16, dev)
+        if out.shape != q.shape:
+            raise ValueError("out must have the shape of q")
+    if lse is None:
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=dev)
+    else:
+        _check(lse, "lse", torch.float32, dev)
+        if tuple(lse.shape) != lse_shape:
+            raise ValueError(f"lse must be {lse_shape}")
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+            int(B), int(H), int(N), int(d), ctypes.c_float(scale), int(bool(causal)),
+            cu_ptr, ctypes.c_void_p(s.cuda_stream))
+    with torch.cuda.device(dev):
+        if exp_mode is None and rescale_mode is None:
+            rc = lib.fa_fwd(*args)
+        else:
+            rc = lib.fa_fwd_variant(*args, int(EXP_HW if exp_mode is None else exp_mode),
+                                    int(RESCALE_STRICT if rescale_mode is None else rescale_mode))
+    if rc != 0:
+        raise FaError(rc, strerror(rc))
+    return out, lse
+
+
+def tile_rows(d: int) -> int:
+    return int(load().fa_tile_rows(int(d)))
+
+
+def tile_keys(d: int) -> int:
+    return int(load().fa_tile_keys(int(d)))

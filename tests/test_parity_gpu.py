@@ -1,0 +1,151 @@
+"""HIP path vs the fp64 oracle, through the C ABI (needs an MI355X).
+
+Small shapes are compared element by element; the library's full-size runs
+(mid, long causal, packed causal, wide-logit at d = 64/128/256) on sampled
+rows that the oracle computes one by one, plus whole-output properties."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_107_amd import fa
+from exact_attention_107_amd.workloads import RUNS, Run, make_inputs
+from gpu_helpers import (assert_within, from_dev, full_parity, run_gpu, sampled_parity,
+                         to_dev)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = Run("small", 2, 3, 300, 128, False, 77)
+
+
+def _small(d, causal, N=300, B=2, H=3, seed=77, sigma=1.0, boost=0.0):
+    r = Run("small", B, H, N, d, causal, seed, sigma_qk=sigma, boost_frac=boost)
+    return make_inputs(r)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_ragged(d, causal):
+    """Several query and key tiles with ragged tails, every element."""
+    m, _ = full_parity(_small(d, causal))
+    print(f"d={d} causal={causal} {m}")
+    assert_within(m, f"d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_causal"])
+def test_tiny_run(name):
+    m, _ = full_parity(make_inputs(RUNS[name]))
+    print(name, m)
+    assert_within(m, name)
+
+
+@pytest.mark.parametrize("N", [1, 2, 17, 63, 64, 65, 127, 129, 255, 257])
+@pytest.mark.parametrize("causal", [False, True])
+def test_edge_lengths(N, causal):
+    m, _ = full_parity(_small(128, causal, N=N, B=1, H=2, seed=100 + N))
+    assert_within(m, f"N={N} causal={causal}")
+
+
+@pytest.mark.parametrize("exp_mode", [fa.EXP_HW, fa.EXP_POLY, fa.EXP_MIXED])
+@pytest.mark.parametrize("rescale_mode", [fa.RESCALE_ALWAYS, fa.RESCALE_STRICT,
+                                          fa.RESCALE_THRESHOLD])
+@pytest.mark.parametrize("causal", [False, True])
+def test_variants(exp_mode, rescale_mode, causal):
+    """Every exp evaluation x rescale policy on a wide-logit input."""
+    inp = _small(128, causal, N=517, B=1, H=2, seed=5, sigma=3.0, boost=0.01)
+    m, _ = full_parity(inp, exp_mode=exp_mode, rescale_mode=rescale_mode)
+    print(exp_mode, rescale_mode, causal, m)
+    assert_within(m, f"exp={exp_mode} rescale={rescale_mode} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_packed_small(causal):
+    lengths = [1, 0, 5, 130, 257, 64, 300]
+    r = Run("packed", len(lengths), 3, 0, 128, causal, 55, varlen=True)
+    inp = make_inputs(r, lengths=lengths)
+    m, _ = full_parity(inp)
+    assert_within(m, f"packed causal={causal}")
+
+
+@pytest.mark.parametrize("d", [64, 256])
+def test_packed_head_dims(d):
+    lengths = [33, 200, 129]
+    r = Run("packed", len(lengths), 2, 0, d, True, 56, varlen=True)
+    m, _ = full_parity(make_inputs(r, lengths=lengths))
+    assert_within(m, f"packed d={d}")
+
+
+def test_packed_equals_dense_bitwise():
+    r = Run("one", 1, 4, 700, 128, True, 9)
+    dense = make_inputs(r)
+    packed = dict(dense)
+    packed["q"], packed["k"], packed["v"] = (dense[x][0] for x in ("q", "k", "v"))
+    packed["cu_seqlens"] = np.array([0, 700], dtype=np.int32)
+    o1, l1 = run_gpu(dense)
+    o2, l2 = run_gpu(packed)
+    assert torch.equal(o1[0].view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1[0], l2)
+
+
+def test_deterministic_bitwise():
+    inp = _small(128, True, N=1000, B=2, H=4, seed=3)
+    o1, l1 = run_gpu(inp)
+    o2, l2 = run_gpu(inp)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+def test_causal_future_independence_bitwise():
+    inp = _small(128, True, N=600, B=1, H=2, seed=4)
+    o1, l1 = run_gpu(inp)
+    cut = 300
+    inp2 = dict(inp)
+    rng = np.random.Generator(np.random.PCG64(8))
+    for x in ("k", "v"):
+        a = inp[x].copy()
+        a[:, cut + 1:] = rng.integers(0, 1 << 14, size=a[:, cut + 1:].shape, dtype=np.uint16)
+        inp2[x] = a
+    o2, l2 = run_gpu(inp2)
+    assert torch.equal(o1[:, :cut + 1].view(torch.int16), o2[:, :cut + 1].view(torch.int16))
+    assert torch.equal(l1[:, :, :cut + 1], l2[:, :, :cut + 1])
+
+
+def test_outputs_fully_written():
+    """NaN-poisoned outputs: every element of O and LSE is overwritten."""
+    inp = _small(128, True, N=333, B=2, H=3, seed=6)
+    q, k, v = (to_dev(inp[x]) for x in ("q", "k", "v"))
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((2, 3, 333), float("nan"), device="cuda")
+    fa.fwd(q, k, v, causal=True, scale=inp["scale"], out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+    assert torch.isfinite(lse).all()
+
+
+def test_lse_normalises_scores():
+    """sum_j exp(scale q.k_j - LSE_i) = 1 in fp64 from the GPU's LSE."""
+    inp = _small(64, True, N=200, B=1, H=1, seed=12)
+    _, lse = run_gpu(inp)
+    from exact_attention_107_amd.workloads import bf16_to_f32
+    Q = bf16_to_f32(inp["q"][0, :, 0]).astype(np.float64)
+    K = bf16_to_f32(inp["k"][0, :, 0]).astype(np.float64)
+    S = (Q @ K.T) * float(np.float32(inp["scale"]))
+    S = np.where(np.tril(np.ones((200, 200), bool)), S, -np.inf)
+    tot = np.exp(S - lse.cpu().numpy()[0, 0][:, None].astype(np.float64)).sum(axis=1)
+    assert np.max(np.abs(tot - 1.0)) < 2e-3
+
+
+FULL_RUNS = ["mid", "mid_causal", "long_causal", "varlen_causal", "wide", "wide_d64",
+             "wide_d256"]
+
+
+@pytest.mark.parametrize("name", FULL_RUNS)
+def test_full_size_run(name):
+    """The full-size runs: sampled rows vs the oracle, whole output finite."""
+    inp = make_inputs(RUNS[name])
+    o, lse = run_gpu(inp)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    m = sampled_parity(inp, o, lse)
+    print(name, m)
+    assert_within(m, name)
