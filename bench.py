@@ -24,8 +24,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense BF16 flop/clk/CU (the 2.5 PF spec)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fa_fwd_wide.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_107_amd", "csrc", "fa_fwd.hip"),
-                  os.path.join(ROOT, "exact_attention_107_amd", "build.py")]
+KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_107_amd", "csrc", f)
+                  for f in ("fa_kernel.hpp", "fa_internal.h", "fa_kernels_d64.hip",
+                            "fa_kernels_d128.hip", "fa_kernels_d256.hip", "fa_api.hip")] + \
+                 [os.path.join(ROOT, "exact_attention_107_amd", "build.py")]
 
 
 def kernel_fingerprint() -> str:
@@ -126,6 +128,9 @@ def main() -> int:
     ap.add_argument("--extra", type=int, default=1, help="also time the other runs and variants")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a known-size "
+                         "reference dispatch for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -156,6 +161,13 @@ def main() -> int:
     def launch():
         fa.fwd(q, k, v, causal=inp["causal"], scale=inp["scale"], cu_seqlens=cu, out=o, lse=lse)
 
+    if args.copy_mb:
+        src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     log(f"[bench] timing {args.steps} steps after {args.warmup} warmup")
     ms_step, ms_kernel, ms_med, ms_min = time_launches(launch, args.steps, args.warmup, torch)
     value = f / (ms_step * 1e-3) / 1e12

@@ -1,43 +1,75 @@
-"""Build libfa.so (the HIP kernels and the C ABI) in-tree with hipcc for gfx950."""
+"""Build libfa.so (HIP kernels for gfx950 + the C ABI) in-tree with hipcc.
+
+One translation unit per head dimension is compiled in parallel, then linked
+with the C ABI unit into exact_attention_107_amd/libfa.so.
+"""
 from __future__ import annotations
 
 import os
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
-SOURCES = [os.path.join(PKG, "csrc", "fa_fwd.hip")]
 LIB_PATH = os.path.join(PKG, "libfa.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
+COMMON = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed fp32 VALU instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # keep MFMA accumulators in architectural VGPRs, where the softmax
-    # rescale and the epilogue operate on them in place
-    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
-    "-I", INCLUDE,
+    "-I", INCLUDE, "-I", CSRC,
 ]
+# Keep MFMA accumulators in architectural VGPRs, where the softmax rescale and
+# the epilogue operate on them in place.  Not for d = 256, whose accumulators
+# do not fit beside the other operands and take the accumulation registers.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+UNITS = [
+    ("fa_kernels_d64.hip", VGPR_FORM),
+    ("fa_kernels_d128.hip", VGPR_FORM),
+    ("fa_kernels_d256.hip", []),
+    ("fa_api.hip", []),
+]
+SOURCES = [os.path.join(CSRC, u) for u, _ in UNITS] + [os.path.join(CSRC, "fa_kernel.hpp"),
+                                                       os.path.join(CSRC, "fa_internal.h")]
+
+
+def _clean(stderr: str) -> str:
+    return "\n".join(l for l in stderr.splitlines()
+                     if "packed-fp32-ops' is not a recognized feature" not in l)
 
 
 def build(verbose: bool = False) -> str:
-    tmp = LIB_PATH + ".tmp"
-    cmd = [HIPCC, *FLAGS, *SOURCES, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    err = "\n".join(l for l in res.stderr.splitlines()
-                    if "packed-fp32-ops' is not a recognized feature" not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if err.strip() and verbose:
-        print(err, file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
+    with tempfile.TemporaryDirectory(prefix="fa_build_") as tmp:
+        procs, objs = [], []
+        for unit, extra in UNITS:
+            obj = os.path.join(tmp, unit.replace(".hip", ".o"))
+            cmd = [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, unit), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((unit, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                 stderr=subprocess.PIPE, text=True)))
+            objs.append(obj)
+        failed = []
+        for unit, p in procs:
+            _, err = p.communicate()
+            if p.returncode != 0:
+                failed.append(f"{unit}:\n{_clean(err)}")
+            elif verbose and _clean(err).strip():
+                print(_clean(err), file=sys.stderr)
+        if failed:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
+        out_tmp = LIB_PATH + ".tmp"
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", out_tmp]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"link failed:\n{_clean(res.stderr)}")
+        os.replace(out_tmp, LIB_PATH)
     return LIB_PATH
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,765 @@
+// Device code of the fused exact-attention forward for gfx950, included by one
+// translation unit per head dimension (fa_kernels_d*.hip).
+// Fused exact-attention forward for AMD Instinct MI355X (gfx950 / CDNA4).
+//
+// O = softmax(Q K^T * scale) V with the online softmax of the FlashAttention-1
+// derivation ("FlashAttention 1-4 explained", online softmax equation block):
+// per query row the kernel carries the running max m, the running sum l and
+// the unnormalised output, and divides by l once at the end (FlashAttention-2
+// deferred normalisation).  S and P live only in registers.
+//
+// Mapping onto CDNA4:
+//  * Each wave owns 32 query rows.  Scores are computed transposed,
+//    S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K (from LDS) is the A
+//    operand and Q (held in VGPRs for the whole kernel) the B operand.  In the
+//    32x32 accumulator layout lane l holds column l%32, i.e. one query row, so
+//    the row max and row sum are in-lane reductions plus one exchange between
+//    lanes l and l+32 (v_permlane32_swap).
+//  * The P tile is converted to bf16 in place and is directly the B operand
+//    of O^T += V^T P^T: its register order fixes a permutation of the 16 keys
+//    of each MFMA, and V is read from LDS in that order with the transposing
+//    ds_read_b64_tr_b16, so P never leaves the VGPRs.  The O^T accumulator
+//    again gives each lane one query row, so the rescale by exp(m_old - m_new)
+//    is a per-lane scalar multiply.
+//  * K and V tiles are staged global -> VGPR -> LDS, double-buffered: the
+//    global loads of tile j+1 are in flight while tile j is computed.  The
+//    LDS rows are padded so that both the K reads (8 lanes, 8 rows, one
+//    16-byte chunk) and the transposing V reads (16 lanes, 4 rows, 32 bytes)
+//    touch distinct banks.
+//  * exp is evaluated as exp2 of (s * scale * log2 e - m) with the hardware
+//    v_exp_f32, or with a degree-3 polynomial on the FMA units (section 3.2
+//    of the FlashAttention V4 explainer), or half and half.
+//  * Conditional rescale (FlashAttention-4 section of the 1-4 post): a wave
+//    skips the O multiply when no row max grew, or, in threshold mode, keeps
+//    its reference max until a row max exceeds it by more than 8.
+//  * Causal tiles that are fully masked are never visited (FlashAttention-2
+//    engineering notes); the tile order puts the longest tiles first and keeps
+//    the work items of one (sequence, head) on one XCD so that its K/V stream
+//    is shared through that XCD's L2.
+//
+// Every function of the library's C ABI is declared in include/fa.h.
+
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "fa.h"
+#include "fa_internal.h"
+
+namespace fa_detail {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T *)(p))
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+// Threshold rescale: P~ = 2^(s*c - m) may reach 2^kTau before m moves.
+constexpr float kTau = 8.0f;
+
+
+// ---------------------------------------------------------------------------
+// exp2 evaluations
+
+// 2^x with x = n + f, n = floor(x), f in [0, 1): p(f) = 1 + f(c1 + f(c2 + f c3))
+// is a minimax fit of 2^f with p(0) = 1 exactly (coefficients derived by
+// gen_exp2_poly.py, max relative error 8.6e-5), and 2^n is added to the
+// exponent field.  x is clamped to -127 first: there n = -127, p = 1 and the
+// sum of the fields is exactly +0, so masked (-inf) scores give 0 and the
+// exponent add never wraps.
+__device__ __forceinline__ float exp2_poly(float x) {
+    x = fmaxf(x, -127.0f);
+    const float n = __builtin_floorf(x);
+    const float f = x - n;
+    float p = __builtin_fmaf(f, 7.706703991e-02f, 2.276449949e-01f);
+    p = __builtin_fmaf(f, p, 6.951167583e-01f);
+    p = __builtin_fmaf(f, p, 1.0f);
+    const int bits = __float_as_int(p) + (static_cast<int>(n) << 23);
+    return __int_as_float(bits);
+}
+
+template <int EXPM>
+__device__ __forceinline__ float exp2_sel(float x, int idx) {
+    if constexpr (EXPM == FA_EXP_HW) {
+        return __builtin_amdgcn_exp2f(x);
+    } else if constexpr (EXPM == FA_EXP_POLY) {
+        return exp2_poly(x);
+    } else {
+        return (idx & 1) ? exp2_poly(x) : __builtin_amdgcn_exp2f(x);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// LDS tile layouts (the LDS has 64 banks of 4 bytes = 16 groups of 16 bytes).
+// Tiles are filled by direct global->LDS loads, each writing 64 lanes x 16
+// bytes contiguously; where a lane's 16 bytes land is fixed, so layouts are
+// chosen by which global chunk each lane fetches.
+//  * K, in planes of 8 chunks: chunks 8p..8p+7 of the 64 rows form plane p
+//    (64 rows x 128 bytes), and within a row the chunks are XOR-permuted by
+//    g(r) = (r >> 1) & 7.  A K fragment read (16 lanes per cycle, 16
+//    consecutive rows, one chunk) then covers all 16 bank groups: row parity
+//    picks the half of the 64 banks, g(r) the group within it.  Each direct
+//    load covers 8 whole rows of a plane (8 x 128 contiguous global bytes).
+//  * V, row-major with the 16-byte chunks of row r XOR-permuted by f_V(r).
+//    The transposing 8-byte V read serves 32 lanes per cycle covering 4
+//    consecutive rows x 4 consecutive chunks; f_V gives the 4 rows disjoint
+//    sets of 4 bank groups.
+
+template <int D> struct Swz {
+    static constexpr int RB = D * 2;  // bytes per row
+    static __device__ __forceinline__ int gk(int r) { return (r >> 1) & 7; }
+    static __device__ __forceinline__ int fv(int r) {
+        if constexpr (D == 64) return ((r >> 1) & 1) << 2;  // 8 chunks/row: rows pair up in 16 groups
+        else return (r & 3) << 2;
+    }
+};
+
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 word 3); loads past
+// the end return zeros (also into LDS) and stores past the end are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, long long bytes) {
+    const long long lim = bytes < 0 ? 0 : (bytes > 0xffffffffLL ? 0xffffffffLL : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
+                                             static_cast<int>(static_cast<uint32_t>(lim)),
+                                             0x00020000);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Transposing LDS read, issued through inline assembly: the compiler then
+// does not treat it as a possible reader of the direct global->LDS loads in
+// flight (it would otherwise wait for all of them first).  The caller owns
+// the LDS wait: lgkm_wait<N>(v) waits until at most N LDS operations are
+// outstanding and ties the wait to v, so uses of v stay after it.
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (const __attribute__((address_space(3))) char *)(p)));
+}
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_read_tr16(uint32_t addr) {
+    u32x2 v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+// Keeps the computation of v inside the current scheduling region: the empty
+// volatile asm consumes v, and volatile asm statements keep their order
+// relative to the region boundaries.
+__device__ __forceinline__ void anchor(float v) { asm volatile("" ::"v"(v)); }
+
+template <int N>
+__device__ __forceinline__ void lgkm_wait(bf16x8 &v) {
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "i"(N));
+}
+
+// Max of x over lanes l and l ^ 32.
+__device__ __forceinline__ float xhalf_max(float x) {
+    const uint32_t u = __float_as_uint(x);
+    auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+__device__ __forceinline__ float xhalf_sum(float x) {
+    const uint32_t u = __float_as_uint(x);
+    auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Work decode: one workgroup = (sequence b, head h, query tile qt).
+
+struct Work {
+    int b, h, qt, n;  // n: length of sequence b
+    long long t0;     // first token of sequence b
+};
+
+template <bool CAUSAL, bool VARLEN, int BR>
+__device__ __forceinline__ bool decode_work(const Params &p, Work &w) {
+    const int wg = blockIdx.x;
+    if constexpr (!VARLEN) {
+        const int BH = p.B * p.H;
+        int bh, qt;
+        if constexpr (CAUSAL) {
+            // longest tiles (highest query tile) first; wg % 8 picks the XCD,
+            // so with BH % 8 == 0 all tiles of one head stay on one XCD
+            qt = p.n_qt - 1 - wg / BH;
+            bh = wg % BH;
+        } else {
+            // equal work: give each XCD a contiguous run of items so the
+            // workgroups resident on one XCD stream the same head's K/V
+            const int G = gridDim.x, x = wg & 7, s = wg >> 3;
+            const int per = G >> 3, rem = G & 7;
+            const int item = x * per + (x < rem ? x : rem) + s;
+            bh = item / p.n_qt;
+            qt = item - bh * p.n_qt;
+        }
+        w.b = bh / p.H;
+        w.h = bh - w.b * p.H;
+        w.qt = qt;
+        w.n = p.N;
+        w.t0 = static_cast<long long>(w.b) * p.N;
+        return true;
+    } else {
+        // Items are (sequence, query tile) pairs ordered by query-tile index,
+        // highest first (for causal masks the work of a tile grows with its
+        // index); ties in sequence order.  Each wave decodes independently
+        // with ballots over up to 64 sequences at a time.
+        const int lane = threadIdx.x & 63;
+        w.h = wg % p.H;
+        int r = wg / p.H;
+        int lmax = 0;
+        for (int base = 0; base < p.B; base += 64) {
+            const int b = base + lane;
+            int nt = 0;
+            if (b < p.B) nt = (p.cu[b + 1] - p.cu[b] + BR - 1) / BR;
+            for (int off = 32; off > 0; off >>= 1) nt = max(nt, __shfl_xor(nt, off));
+            lmax = max(lmax, __builtin_amdgcn_readfirstlane(nt));
+        }
+        for (int L = lmax - 1; L >= 0; --L) {
+            int cnt = 0;
+            for (int base = 0; base < p.B; base += 64) {
+                const int b = base + lane;
+                bool on = false;
+                if (b < p.B) on = (p.cu[b + 1] - p.cu[b] + BR - 1) / BR > L;
+                cnt += __popcll(__ballot(on));
+            }
+            if (r < cnt) {
+                for (int base = 0; base < p.B; base += 64) {
+                    const int b = base + lane;
+                    bool on = false;
+                    if (b < p.B) on = (p.cu[b + 1] - p.cu[b] + BR - 1) / BR > L;
+                    unsigned long long m = __ballot(on);
+                    const int c = __popcll(m);
+                    if (r < c) {
+                        // position of the r-th set bit of m
+                        for (int i = 0; i < r; ++i) m &= m - 1;
+                        // every value here is wave-uniform; say so to the compiler
+                        const int bsel = __builtin_amdgcn_readfirstlane(
+                            base + __ffsll(static_cast<long long>(m)) - 1);
+                        w.b = bsel;
+                        w.qt = __builtin_amdgcn_readfirstlane(L);
+                        const int s0 = __builtin_amdgcn_readfirstlane(p.cu[bsel]);
+                        const int s1 = __builtin_amdgcn_readfirstlane(p.cu[bsel + 1]);
+                        w.t0 = s0;
+                        w.n = s1 - s0;
+                        return true;
+                    }
+                    r -= c;
+                }
+            }
+            r -= cnt;
+        }
+        return false;  // surplus workgroup of the grid bound
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The kernel.  NW waves x 32 rows = BR query rows per workgroup; BC keys per
+// K/V tile.
+//
+// Each wave runs a two-stage software pipeline over the K/V tiles so that its
+// MFMAs overlap its own softmax arithmetic:
+//   [A_j]  MFMA  S_{j+1} = K_{j+1} Q^T  ||  VALU  P_j = 2^(S_j c - m_j), row sums
+//   [B_j]  MFMA  O^T += V_j^T P_j^T     ||  VALU  O *= alpha_j (when needed),
+//                                              row max of S_{j+1}, m_{j+1}, alpha_{j+1}
+// LDS holds two K and two V tiles.  At the start of iteration j the direct
+// loads of K_{j+2} and V_{j+1} are issued into the tiles of K_j and V_{j-1}
+// (both consumed before the previous barrier); the barrier that ends the
+// iteration makes them visible.  LDS fragments are read one MFMA ahead.
+
+template <int D, int BC, int NW, bool CAUSAL, bool VARLEN, int EXPM, int RSM>
+__global__ void __launch_bounds__(NW * 64)
+fa_fwd_kernel(Params p) {
+    using SW = Swz<D>;
+    constexpr int BR = NW * 32;
+    constexpr int KK = D / 16;           // MFMA k-steps of Q K^T
+    constexpr int NKB = BC / 32;         // 32-key blocks per tile
+    constexpr int NDB = D / 32;          // 32-wide d blocks of O^T
+    constexpr int NT16 = BC / 16;        // 16-key chunks (PV k-steps)
+    constexpr int RB = SW::RB;
+    constexpr int TB = BC * RB;          // bytes per K (or V) tile
+    constexpr int BLK = TB / 1024;       // 1 KB direct-load blocks per tile
+    constexpr int BPW = BLK / NW;        // blocks per wave per tile
+    constexpr int MS = KK * NKB;         // MFMAs of one S tile (= of one PV pass)
+    constexpr int NE = NKB * 16;         // S elements per lane
+    constexpr int EPS = NE / MS;         // S elements exponentiated per S MFMA
+    static_assert(BLK % NW == 0, "tile must split evenly over waves");
+    static_assert(NE % MS == 0 && MS == NT16 * NDB, "phase shapes");
+
+    // Two K and two V tiles, as separate objects so that the compiler can see
+    // that reads of one tile never alias the direct loads filling another.
+    __shared__ __attribute__((aligned(1024))) char k_lds0[TB], k_lds1[TB], v_lds0[TB], v_lds1[TB];
+
+    Work w;
+    if (!decode_work<CAUSAL, VARLEN, BR>(p, w)) return;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int c = lane & 31, hh = lane >> 5;
+    const int n = w.n;
+    const int q0 = w.qt * BR;
+    const long long rs = static_cast<long long>(p.H) * D;  // token stride (elements)
+    const long long base = (w.t0 * p.H + w.h) * D;
+    const uint16_t *qg = p.q + base;
+    const uint16_t *kg = p.k + base;
+    const uint16_t *vg = p.v + base;
+
+    const int wrow0 = q0 + wave * 32;  // first row of this wave
+    const int qrow = wrow0 + c;        // this lane's row
+
+    // Q fragments: B operand of S^T = K Q^T, lane (c, hh) holds
+    // Q[qrow][kk*16 + hh*8 .. +8]; rows >= n read as zeros.
+    bf16x8 qf[KK];
+    {
+        const auto qrs = make_rsrc(qg + wrow0 * rs, (long long)(n - wrow0) * rs * 2);
+        const int voff = (c * static_cast<int>(rs) + hh * 8) * 2;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            qf[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, voff + kk * 32, 0, 0));
+    }
+
+    const int kv_end = CAUSAL ? min(n, q0 + BR) : n;
+    const int nkv = (kv_end + BC - 1) / BC;
+    // tiles this wave computes: the causal diagonal ends its work earlier
+    const int nkv_w = CAUSAL ? min(nkv, (wrow0 + 31) / BC + 1) : nkv;
+
+    // ---- direct global -> LDS loads ---------------------------------------------
+    // K: the tile is 8*D/64 loads of 1 KB (8 rows of one 128-byte plane each);
+    // wave w issues loads w, w + NW, ...  Lane l of load I fills row
+    // 8 (I % 8) + l / 8 of plane I / 8, slot l % 8, with logical chunk
+    // (l % 8) ^ g(row); g depends on I only through I % 2, which is the same
+    // for all of a wave's loads, so one per-lane offset serves them all.
+    // V: wave w fills 1 KB blocks w, w + NW, ...; lane l of block b fills tile
+    // bytes b*1024 + 16 l = chunk slot pc of row r with logical chunk pc ^ f_V(r)
+    // (f_V depends only on l).
+    static_assert(BC == 64, "K planes are 64 rows");
+    static_assert(NW == 4 || NW == 8, "each wave's K loads must share one row parity");
+    constexpr int KLD = D / 8;           // 1 KB K loads per tile
+    constexpr int KPW = KLD / NW;        // K loads per wave
+    const int rs_bytes = static_cast<int>(rs) * 2;
+    int koff;
+    {
+        const int r = 8 * (wave % 8) + lane / 8;
+        koff = r * rs_bytes + (((lane % 8) ^ Swz<D>::gk(r)) << 4);
+    }
+    int voff;
+    {
+        const int pos = wave * 1024 + lane * 16;
+        const int r = pos / RB, pc = (pos % RB) / 16;
+        voff = r * rs_bytes + ((pc ^ Swz<D>::fv(r)) << 4);
+    }
+    auto dma_k = [&](char *tile, int j) {
+        const int kv0 = j * BC;
+        const auto rsrc = make_rsrc(kg + kv0 * rs, (long long)(n - kv0) * rs_bytes);
+#pragma unroll
+        for (int i = 0; i < KPW; ++i) {
+            const int I = wave + NW * i;              // load index within the tile
+            const int di = (I % 8) - (wave % 8);      // rows of this load past the wave's first
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, tile + I * 1024), 16, koff,
+                                                     8 * di * rs_bytes + (I / 8) * 128, 0, 0);
+        }
+    };
+    constexpr int VROWS = 1024 / RB;     // V rows per 1 KB block
+    auto dma_v = [&](char *tile, int j) {
+        const int kv0 = j * BC;
+        const auto rsrc = make_rsrc(vg + kv0 * rs, (long long)(n - kv0) * rs_bytes);
+#pragma unroll
+        for (int i = 0; i < BPW; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, tile + (wave + NW * i) * 1024), 16,
+                                                     voff, NW * i * VROWS * rs_bytes, 0, 0);
+    };
+
+    // ---- LDS fragment reads --------------------------------------------------------
+    // K fragment of S MFMA (kk, kb2): row kb2*32 + c, chunk 2 kk + hh, i.e.
+    // plane kk / 4, in-plane chunk 2 (kk % 4) + hh.
+    int kaddr[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) kaddr[b] = c * 128 + (((2 * b + hh) ^ Swz<D>::gk(c)) << 4);
+    auto kfrag = [&](const char *kb, int kk, int kb2) -> bf16x8 {
+        return *reinterpret_cast<const bf16x8 *>(kb + kaddr[kk % 4] + (kk / 4) * 8192 + kb2 * 32 * 128);
+    };
+    // V fragment of PV MFMA (t, db): rows t*16 + hh*4 + s/4 (+8 for the upper
+    // half), columns db*32 + (g&1)*16 + (s&3)*4, for lane group g, s = lane%16.
+    const int g16 = lane >> 4, s16 = lane & 15;
+    constexpr int NVA = NDB < 4 ? NDB : 4;
+    int vaddr[NVA];
+    {
+        const int vr = hh * 4 + (s16 >> 2);
+        const int x = (g16 & 1) * 2 + ((s16 & 3) >> 1);
+#pragma unroll
+        for (int b = 0; b < NVA; ++b)
+            vaddr[b] = vr * RB + (((4 * b + x) ^ Swz<D>::fv(vr)) << 4) + (s16 & 1) * 8;
+    }
+    // Issues the two transposing reads of a V fragment; the caller waits.
+    auto vfrag_issue = [&](const char *vb, auto t_, auto db_) -> bf16x8 {
+        constexpr int t = decltype(t_)::value, db = decltype(db_)::value;
+        const uint32_t a = lds_offset(vb) + vaddr[db % NVA];
+        constexpr int off = (db / NVA) * 256 + t * 16 * RB;
+        const u32x2 lo = ds_read_tr16<off>(a);
+        const u32x2 hi = ds_read_tr16<off + 8 * RB>(a);
+        const u32x4 both = {lo[0], lo[1], hi[0], hi[1]};
+        return __builtin_bit_cast(bf16x8, both);
+    };
+
+    // ---- per-wave softmax state ---------------------------------------------------
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
+    float m_run = -INFINITY;  // reference max, scaled log2 units
+    float l_run = 0.0f;       // this lane's partial row sum
+    float m_use = 0.0f;       // subtrahend of the tile being exponentiated
+    float alpha = 1.0f;       // pending rescale of O for that tile
+    bool rescale_o = false;   // wave-uniform: some row's reference moved
+    const float cs = p.cs;
+
+    // -inf for tail keys (>= n) and, when causal, keys after the query.
+    auto need_mask = [&](int j) {
+        const int kv0 = j * BC;
+        return (CAUSAL && kv0 + BC - 1 > wrow0) || kv0 + BC > n;
+    };
+    auto s_mask = [&](f32x16 (&s)[NKB], int j) {
+        const int kv0 = j * BC;
+#pragma unroll
+        for (int kb2 = 0; kb2 < NKB; ++kb2) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = kv0 + kb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+                const bool off = key >= n || (CAUSAL && key > qrow);
+                s[kb2][r] = off ? -INFINITY : s[kb2][r];
+            }
+        }
+    };
+    // Reference max update from a tile's raw row max.
+    auto s_update = [&](float mx) {
+        mx = xhalf_max(mx);
+        const float mt = (mx == -INFINITY) ? -INFINITY : mx * cs;
+        float m_new;
+        bool grow;
+        if constexpr (RSM == FA_RESCALE_THRESHOLD) {
+            grow = mt > m_run + kTau;  // also true for the first finite tile
+            m_new = grow ? mt : m_run;
+        } else {
+            m_new = fmaxf(m_run, mt);
+            grow = m_new > m_run;
+        }
+        m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+        alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 1 if unchanged, 0 from -inf
+        if constexpr (RSM == FA_RESCALE_ALWAYS) {
+            rescale_o = true;
+        } else {
+            rescale_o = __ballot(grow) != 0;
+        }
+        l_run *= alpha;
+        m_run = m_new;
+    };
+    auto s_rowmax = [&](const f32x16 (&s)[NKB]) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb2][r]);
+        return mx;
+    };
+    // S^T = K Q^T alone (prologue and pipeline edges).
+    auto s_mfma = [&](f32x16 (&s)[NKB], const char *kb) {
+#pragma unroll
+        for (int i = 0; i < NKB; ++i) s[i] = f32x16{};
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            const int kb2 = m / KK, kk = m % KK;
+            s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(kb, kk, kb2), qf[kk], s[kb2], 0, 0, 0);
+        }
+    };
+    // P~ element e (0..NE-1) of S; e = kb2*16 + r, and pf[t] holds e = 8t..8t+7.
+    bf16x8 pf[NT16];
+    float pe[NE];
+    auto p_elem = [&](const f32x16 (&s)[NKB], int e) {
+        pe[e] = exp2_sel<EXPM>(__builtin_fmaf(s[e >> 4][e & 15], cs, -m_use), e);
+    };
+    auto p_pack = [&](int t, float &rsum) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+            rsum += pe[8 * t + i] + pe[8 * t + i + 1];
+            pk[i >> 1] = pack_bf16x2(pe[8 * t + i], pe[8 * t + i + 1]);
+        }
+        u32x4 pv = {pk[0], pk[1], pk[2], pk[3]};
+        pf[t] = __builtin_bit_cast(bf16x8, pv);
+    };
+    auto p_exp = [&](const f32x16 (&s)[NKB]) {
+        float rsum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            p_elem(s, e);
+            if ((e & 7) == 7) p_pack(e >> 3, rsum);
+        }
+        l_run += rsum;
+    };
+    auto o_rescale = [&](float a) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= a;
+    };
+    // PV product: O^T += V^T P^T, MFMA order t-major (all d blocks of key
+    // chunk t, then chunk t+1), V fragments read two MFMAs ahead.  `work(m)`
+    // is VALU work placed after MFMA m; it may produce pf[t] for a later t.
+    auto pv_run = [&](const char *vb, auto &&work) {
+        bf16x8 vf[MS];
+        static_for<0, (MS < 2 ? MS : 2)>([&](auto m) {
+            vf[m] = vfrag_issue(vb, std::integral_constant<int, m / NDB>{},
+                                std::integral_constant<int, m % NDB>{});
+        });
+        static_for<0, MS>([&](auto m) {
+            constexpr int t = m / NDB, db = m % NDB;
+            if constexpr (m + 1 < MS) lgkm_wait<2>(vf[m]);
+            else lgkm_wait<0>(vf[m]);
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[m], pf[t], oacc[db], 0, 0, 0);
+            if constexpr (m + 2 < MS)
+                vf[m + 2] = vfrag_issue(vb, std::integral_constant<int, (m + 2) / NDB>{},
+                                        std::integral_constant<int, (m + 2) % NDB>{});
+            work(m);
+        });
+    };
+    auto pv_mfma = [&](const char *vb) { pv_run(vb, [](auto) {}); };
+
+    // The exponentials of S_j are split between the two phases: [A] does key
+    // chunks 0 .. NT16/2-1 (one element per S MFMA), [B] the rest, chunk
+    // NT16/2 + i during PV MFMAs i*NDB .. (i+1)*NDB-1, i.e. before the first
+    // MFMA that needs it.  [B] then takes the row max of S_{j+1}.  The
+    // sched_group_barrier sequences spread the VALU work evenly between the
+    // MFMAs (a wave issues in order; a burst of exponentials between two MFMAs
+    // would hold back the second).
+    constexpr int HALF = NE / 2;          // elements per phase
+    // [A]: S MFMA m takes elements [m*HALF/MS, (m+1)*HALF/MS)
+
+    // [A]: S_{j+1} MFMAs interleaved with the first half of the exponentials
+    // of S_j.
+    float rsum_a = 0.0f;
+    auto phase_a = [&](f32x16 (&nxt)[NKB], const f32x16 (&cur)[NKB], const char *kb) {
+#pragma unroll
+        for (int i = 0; i < NKB; ++i) nxt[i] = f32x16{};
+        float rsum = 0.0f;
+        bf16x8 kf[3];
+        // MFMA order alternates the NKB accumulator chains
+        kf[0] = kfrag(kb, 0, 0);
+        if constexpr (MS > 1) kf[1] = kfrag(kb, 1 / NKB, 1 % NKB);
+        static_for<0, MS>([&](auto m) {
+            constexpr int kb2 = m % NKB, kk = m / NKB;
+            if constexpr (m + 2 < MS) kf[(m + 2) % 3] = kfrag(kb, (m + 2) / NKB, (m + 2) % NKB);
+            nxt[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[m % 3], qf[kk], nxt[kb2], 0, 0, 0);
+#pragma unroll
+            for (int e = m * HALF / MS; e < (m + 1) * HALF / MS; ++e) {
+                p_elem(cur, e);
+                anchor(pe[e]);
+                if ((e & 7) == 7) p_pack(e >> 3, rsum);
+            }
+        });
+        anchor(rsum);
+        __builtin_amdgcn_sched_group_barrier(0x100, MS > 1 ? 2 : 1, 0);  // first K fragments
+        static_for<0, MS>([&](auto m) {
+            constexpr int ne = (m + 1) * HALF / MS - m * HALF / MS;  // elements of this step
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            if constexpr (m + 2 < MS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+            if constexpr (ne > 0) __builtin_amdgcn_sched_group_barrier(0x402, 3 * ne + (ne + 1) / 2, 0);
+        });
+        rsum_a = rsum;
+    };
+    // [B]: PV MFMAs interleaved with the second half of the exponentials of
+    // S_j and the row max of S_{j+1}.
+    auto phase_b = [&](const f32x16 (&nxt)[NKB], const f32x16 (&cur)[NKB], const char *vb) {
+        constexpr int EB = 8 / NDB;                 // elements per MFMA, first half of [B]
+        constexpr int MB = NE / (MS - MS / 2);      // max elements per MFMA, second half
+        static_assert(8 % NDB == 0 && NE % (MS - MS / 2) == 0, "element split");
+        float rsum = rsum_a;
+        float mx = -INFINITY;
+        pv_run(vb, [&](auto m) {
+            if constexpr (m < MS / 2) {
+#pragma unroll
+                for (int i = 0; i < EB; ++i) {
+                    const int e = HALF + m * EB + i;
+                    p_elem(cur, e);
+                    if ((e & 7) == 7) p_pack(e >> 3, rsum);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < MB; ++i) {
+                    const int e = (m - MS / 2) * MB + i;
+                    mx = fmaxf(mx, nxt[e >> 4][e & 15]);
+                }
+            }
+        });
+        static_for<0, MS>([&](auto m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            if constexpr (m < MS / 2) __builtin_amdgcn_sched_group_barrier(0x402, 3 * EB + (EB + 1) / 2, 0);
+            else __builtin_amdgcn_sched_group_barrier(0x402, (MB + 1) / 2, 0);
+        });
+        l_run += rsum;
+        return mx;
+    };
+
+    // ---- prologue: K_0, V_0, K_1 into LDS; S_0 and its row max ------------------
+    f32x16 sa[NKB], sb[NKB];
+    dma_k(k_lds0, 0);
+    dma_v(v_lds0, 0);
+    if (nkv > 1) dma_k(k_lds1, 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (nkv_w > 0) {
+        s_mfma(sa, k_lds0);
+        if (need_mask(0)) s_mask(sa, 0);
+        s_update(s_rowmax(sa));
+    }
+    __syncthreads();  // K tile 0 is reloaded at the start of iteration 0
+
+    // Direct loads that belong to iteration j: K_{j+2} over K_j, V_{j+1} over
+    // V_{j-1} (both consumed before the previous barrier).
+    auto issue_loads = [&](int j, char *k_dst, char *v_dst) {
+        if (j + 2 < nkv) dma_k(k_dst, j + 2);
+        if (j + 1 < nkv) dma_v(v_dst, j + 1);
+    };
+    auto end_iteration = [&]() {
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
+        __syncthreads();
+    };
+    // A full pipeline iteration (tiles j and j+1 both computed by this wave);
+    // PAR = j & 1 selects the LDS tiles statically.  MASK: tile j+1 needs the
+    // tail/causal mask (kept out of the hot loop so that nothing separates
+    // phase [A] from phase [B]).
+    auto full_step = [&](auto par, auto mask, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB], int j) {
+        constexpr int PAR = decltype(par)::value;
+        issue_loads(j, (PAR ? k_lds1 : k_lds0), (PAR ? v_lds0 : v_lds1));
+        if (rescale_o) o_rescale(alpha);
+        __builtin_amdgcn_sched_barrier(0);
+        phase_a(nxt, cur, (PAR ? k_lds0 : k_lds1));  // K_{j+1}
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (decltype(mask)::value) s_mask(nxt, j + 1);
+        s_update(phase_b(nxt, cur, (PAR ? v_lds1 : v_lds0)));  // V_j
+        __builtin_amdgcn_sched_barrier(0);
+        end_iteration();
+    };
+    // The wave's last tile: no next S.
+    auto drain_step = [&](const f32x16 (&cur)[NKB], int j) {
+        const int par = j & 1;
+        issue_loads(j, (par ? k_lds1 : k_lds0), (par ? v_lds0 : v_lds1));
+        if (rescale_o) o_rescale(alpha);
+        p_exp(cur);
+        pv_mfma((par ? v_lds1 : v_lds0));
+        end_iteration();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using NoMask = std::integral_constant<bool, false>;
+    using Mask = std::integral_constant<bool, true>;
+
+    // first tile that needs a mask (tail: n / BC; causal: (wrow0 + 1) / BC)
+    const int jm = CAUSAL ? min(n / BC, (wrow0 + 1) / BC) : n / BC;
+    const int lim = min(nkv_w, jm);
+    int j = 0;
+    // hot loop: pairs of full steps whose next tiles need no mask
+    for (; j + 2 < lim; j += 2) {
+        full_step(I0{}, NoMask{}, sa, sb, j);
+        full_step(I1{}, NoMask{}, sb, sa, j + 1);
+    }
+    // the wave's last few full steps, masked (a mask on an interior tile
+    // changes nothing); still in pairs so S_j and S_{j+1} keep their registers
+    for (; j + 2 < nkv_w; j += 2) {
+        full_step(I0{}, Mask{}, sa, sb, j);
+        full_step(I1{}, Mask{}, sb, sa, j + 1);
+    }
+    if (j + 1 < nkv_w) {
+        full_step(I0{}, Mask{}, sa, sb, j);
+        ++j;
+    }
+    if (j < nkv_w) {
+        if (j & 1) drain_step(sb, j);
+        else drain_step(sa, j);
+        ++j;
+    }
+    // tiles past this wave's causal horizon: keep loading for the other waves
+    for (; j < nkv; ++j) {
+        issue_loads(j, ((j & 1) ? k_lds1 : k_lds0), ((j & 1) ? v_lds0 : v_lds1));
+        end_iteration();
+    }
+
+    // ---- epilogue: O / l, LSE = (m + log2 l) ln 2 ----------------------------
+    const float l = xhalf_sum(l_run);
+    {
+        // rows >= n fall outside the buffer and are dropped
+        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+        const auto ors = make_rsrc(p.o + base + wrow0 * rs, (long long)(n - wrow0) * rs * 2);
+        const int voff = c * static_cast<int>(rs) * 2;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int col = db * 32 + g4 * 8 + hh * 4;
+                u32x2 v2 = {pack_bf16x2(oacc[db][g4 * 4 + 0] * inv, oacc[db][g4 * 4 + 1] * inv),
+                            pack_bf16x2(oacc[db][g4 * 4 + 2] * inv, oacc[db][g4 * 4 + 3] * inv)};
+                __builtin_amdgcn_raw_buffer_store_b64(v2, ors, voff + col * 2, 0, 0);
+            }
+        }
+    }
+    if (qrow < n) {
+        if (hh == 0) {
+            const float lse = l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+            long long li;
+            if constexpr (VARLEN) {
+                li = static_cast<long long>(w.h) * p.N + w.t0 + qrow;
+            } else {
+                li = (static_cast<long long>(w.b) * p.H + w.h) * p.N + qrow;
+            }
+            p.lse[li] = lse;
+        }
+    }
+}
+
+
+template <int D, bool CAUSAL, bool VARLEN, int EXPM>
+KernelFn select_rsm(int rsm) {
+    constexpr int BC = kTileKeys, NW = kWorkgroupWaves;
+    switch (rsm) {
+        case FA_RESCALE_ALWAYS: return fa_fwd_kernel<D, BC, NW, CAUSAL, VARLEN, EXPM, FA_RESCALE_ALWAYS>;
+        case FA_RESCALE_STRICT: return fa_fwd_kernel<D, BC, NW, CAUSAL, VARLEN, EXPM, FA_RESCALE_STRICT>;
+        default: return fa_fwd_kernel<D, BC, NW, CAUSAL, VARLEN, EXPM, FA_RESCALE_THRESHOLD>;
+    }
+}
+
+template <int D, bool CAUSAL, bool VARLEN>
+KernelFn select_exp(int expm, int rsm) {
+    switch (expm) {
+        case FA_EXP_HW: return select_rsm<D, CAUSAL, VARLEN, FA_EXP_HW>(rsm);
+        case FA_EXP_POLY: return select_rsm<D, CAUSAL, VARLEN, FA_EXP_POLY>(rsm);
+        default: return select_rsm<D, CAUSAL, VARLEN, FA_EXP_MIXED>(rsm);
+    }
+}
+
+template <int D>
+KernelFn select_kernel(bool causal, bool varlen, int expm, int rsm) {
+    if (causal) return varlen ? select_exp<D, true, true>(expm, rsm) : select_exp<D, true, false>(expm, rsm);
+    return varlen ? select_exp<D, false, true>(expm, rsm) : select_exp<D, false, false>(expm, rsm);
+}
+
+}  // namespace fa_detail
