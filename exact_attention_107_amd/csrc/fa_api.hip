@@ -49,7 +49,7 @@ const char *fa_strerror(int code) {
     }
 }
 
-int fa_tile_rows(int d) { return (d == 64 || d == 128 || d == 256) ? kTileRows : 0; }
+int fa_tile_rows(int d) { return tile_rows_for(d); }
 
 int fa_tile_keys(int d) { return (d == 64 || d == 128 || d == 256) ? kTileKeys : 0; }
 
@@ -89,7 +89,8 @@ int fa_fwd_variant(const void *q, const void *k, const void *v, void *o, float *
     prm.H = H;
     prm.N = N;
     prm.cs = scale * kLog2e;
-    const long long n_qt = (static_cast<long long>(N) + kTileRows - 1) / kTileRows;
+    const int rows = tile_rows_for(d);
+    const long long n_qt = (static_cast<long long>(N) + rows - 1) / rows;
     prm.n_qt = static_cast<int>(n_qt);
     long long grid;
     if (varlen) {

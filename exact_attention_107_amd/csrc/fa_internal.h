@@ -19,10 +19,24 @@ struct Params {
 
 using KernelFn = void (*)(Params);
 
-// Launch geometry shared by every instance.
-constexpr int kWorkgroupWaves = 4;               // waves per workgroup
-constexpr int kTileRows = kWorkgroupWaves * 32;  // query rows per workgroup
-constexpr int kTileKeys = 64;                    // keys per K/V tile
+// Launch geometry.  Every instance has 4 waves per workgroup and 64-key K/V
+// tiles; each wave owns kBlocks blocks of 32 query rows.  (Two blocks per wave
+// would let each K/V fragment read from LDS feed two MFMAs, but at d = 128 the
+// kernel then needs more than the 512 registers of a wave.)
+constexpr int kWorkgroupWaves = 4;
+constexpr int kTileKeys = 64;
+template <int D> struct Geometry {
+    static constexpr int kBlocks = 1;
+    static constexpr int kRows = kWorkgroupWaves * 32 * kBlocks;  // query rows per workgroup
+};
+inline int tile_rows_for(int d) {
+    switch (d) {
+        case 64: return Geometry<64>::kRows;
+        case 128: return Geometry<128>::kRows;
+        case 256: return Geometry<256>::kRows;
+        default: return 0;
+    }
+}
 
 // Kernel instance for head dimension D (defined in fa_kernels_d<D>.hip).
 KernelFn select_d64(bool causal, bool varlen, int exp_mode, int rescale_mode);

@@ -275,24 +275,27 @@ __device__ __forceinline__ bool decode_work(const Params &p, Work &w) {
 }
 
 // ---------------------------------------------------------------------------
-// The kernel.  NW waves x 32 rows = BR query rows per workgroup; BC keys per
-// K/V tile.
+// The kernel.  NW waves, each owning QB blocks of 32 query rows, so a
+// workgroup covers BR = NW * QB * 32 rows; BC keys per K/V tile.  With QB = 2
+// every K or V fragment read from LDS feeds two MFMAs.
 //
 // Each wave runs a two-stage software pipeline over the K/V tiles so that its
 // MFMAs overlap its own softmax arithmetic:
-//   [A_j]  MFMA  S_{j+1} = K_{j+1} Q^T  ||  VALU  P_j = 2^(S_j c - m_j), row sums
-//   [B_j]  MFMA  O^T += V_j^T P_j^T     ||  VALU  O *= alpha_j (when needed),
-//                                              row max of S_{j+1}, m_{j+1}, alpha_{j+1}
-// LDS holds two K and two V tiles.  At the start of iteration j the direct
-// loads of K_{j+2} and V_{j+1} are issued into the tiles of K_j and V_{j-1}
-// (both consumed before the previous barrier); the barrier that ends the
-// iteration makes them visible.  LDS fragments are read one MFMA ahead.
+//   [A_j]  MFMA  S_{j+1} = K_{j+1} Q^T  ||  VALU  first half of P_j = 2^(S_j c - m_j)
+//   [B_j]  MFMA  O^T += V_j^T P_j^T     ||  VALU  second half of P_j, row max of
+//                                              S_{j+1}
+// after which the reference max, the rescale factor and l are updated.  LDS
+// holds two K and two V tiles; at the start of iteration j the direct loads
+// of K_{j+2} and V_{j+1} are issued into the tiles of K_j and V_{j-1} (both
+// consumed before the previous barrier); the barrier that ends the iteration
+// makes them visible.
 
-template <int D, int BC, int NW, bool CAUSAL, bool VARLEN, int EXPM, int RSM>
+template <int D, int BC, int NW, int QB, bool CAUSAL, bool VARLEN, int EXPM, int RSM>
 __global__ void __launch_bounds__(NW * 64)
 fa_fwd_kernel(Params p) {
     using SW = Swz<D>;
-    constexpr int BR = NW * 32;
+    constexpr int RW = QB * 32;          // query rows per wave
+    constexpr int BR = NW * RW;          // query rows per workgroup
     constexpr int KK = D / 16;           // MFMA k-steps of Q K^T
     constexpr int NKB = BC / 32;         // 32-key blocks per tile
     constexpr int NDB = D / 32;          // 32-wide d blocks of O^T
@@ -300,12 +303,11 @@ fa_fwd_kernel(Params p) {
     constexpr int RB = SW::RB;
     constexpr int TB = BC * RB;          // bytes per K (or V) tile
     constexpr int BLK = TB / 1024;       // 1 KB direct-load blocks per tile
-    constexpr int BPW = BLK / NW;        // blocks per wave per tile
-    constexpr int MS = KK * NKB;         // MFMAs of one S tile (= of one PV pass)
-    constexpr int NE = NKB * 16;         // S elements per lane
-    constexpr int EPS = NE / MS;         // S elements exponentiated per S MFMA
+    constexpr int BPW = BLK / NW;        // V blocks per wave per tile
+    constexpr int MS = KK * NKB;         // fragment steps of one S tile (= of one PV pass)
+    constexpr int NE = NKB * 16;         // S elements per lane per query block
     static_assert(BLK % NW == 0, "tile must split evenly over waves");
-    static_assert(NE % MS == 0 && MS == NT16 * NDB, "phase shapes");
+    static_assert(MS == NT16 * NDB, "phase shapes");
 
     // Two K and two V tiles, as separate objects so that the compiler can see
     // that reads of one tile never alias the direct loads filling another.
@@ -326,24 +328,26 @@ fa_fwd_kernel(Params p) {
     const uint16_t *kg = p.k + base;
     const uint16_t *vg = p.v + base;
 
-    const int wrow0 = q0 + wave * 32;  // first row of this wave
-    const int qrow = wrow0 + c;        // this lane's row
+    const int wrow0 = q0 + wave * RW;  // first row of this wave; block b starts at wrow0 + 32 b
 
-    // Q fragments: B operand of S^T = K Q^T, lane (c, hh) holds
-    // Q[qrow][kk*16 + hh*8 .. +8]; rows >= n read as zeros.
-    bf16x8 qf[KK];
+    // Q fragments: B operand of S^T = K Q^T, lane (c, hh) of block b holds
+    // Q[wrow0 + 32 b + c][kk*16 + hh*8 .. +8]; rows >= n read as zeros.
+    bf16x8 qf[QB][KK];
     {
         const auto qrs = make_rsrc(qg + wrow0 * rs, (long long)(n - wrow0) * rs * 2);
         const int voff = (c * static_cast<int>(rs) + hh * 8) * 2;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-            qf[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, voff + kk * 32, 0, 0));
+        for (int b = 0; b < QB; ++b)
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                qf[b][kk] = __builtin_bit_cast(
+                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, voff + kk * 32, 32 * b * static_cast<int>(rs) * 2, 0));
     }
 
     const int kv_end = CAUSAL ? min(n, q0 + BR) : n;
     const int nkv = (kv_end + BC - 1) / BC;
     // tiles this wave computes: the causal diagonal ends its work earlier
-    const int nkv_w = CAUSAL ? min(nkv, (wrow0 + 31) / BC + 1) : nkv;
+    const int nkv_w = CAUSAL ? min(nkv, (wrow0 + RW - 1) / BC + 1) : nkv;
 
     // ---- direct global -> LDS loads ---------------------------------------------
     // K: the tile is 8*D/64 loads of 1 KB (8 rows of one 128-byte plane each);
@@ -376,7 +380,7 @@ fa_fwd_kernel(Params p) {
 #pragma unroll
         for (int i = 0; i < KPW; ++i) {
             const int I = wave + NW * i;              // load index within the tile
-            const int di = (I % 8) - (wave % 8);      // rows of this load past the wave's first
+            const int di = (I % 8) - (wave % 8);      // rows of this load past the wave's first / 8
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, tile + I * 1024), 16, koff,
                                                      8 * di * rs_bytes + (I / 8) * 128, 0, 0);
         }
@@ -392,15 +396,15 @@ fa_fwd_kernel(Params p) {
     };
 
     // ---- LDS fragment reads --------------------------------------------------------
-    // K fragment of S MFMA (kk, kb2): row kb2*32 + c, chunk 2 kk + hh, i.e.
+    // K fragment of S step (kk, kb2): rows kb2*32 + c, chunk 2 kk + hh, i.e.
     // plane kk / 4, in-plane chunk 2 (kk % 4) + hh.
     int kaddr[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) kaddr[b] = c * 128 + (((2 * b + hh) ^ Swz<D>::gk(c)) << 4);
+    for (int bb = 0; bb < 4; ++bb) kaddr[bb] = c * 128 + (((2 * bb + hh) ^ Swz<D>::gk(c)) << 4);
     auto kfrag = [&](const char *kb, int kk, int kb2) -> bf16x8 {
         return *reinterpret_cast<const bf16x8 *>(kb + kaddr[kk % 4] + (kk / 4) * 8192 + kb2 * 32 * 128);
     };
-    // V fragment of PV MFMA (t, db): rows t*16 + hh*4 + s/4 (+8 for the upper
+    // V fragment of PV step (t, db): rows t*16 + hh*4 + s/4 (+8 for the upper
     // half), columns db*32 + (g&1)*16 + (s&3)*4, for lane group g, s = lane%16.
     const int g16 = lane >> 4, s16 = lane & 15;
     constexpr int NVA = NDB < 4 ? NDB : 4;
@@ -409,8 +413,8 @@ fa_fwd_kernel(Params p) {
         const int vr = hh * 4 + (s16 >> 2);
         const int x = (g16 & 1) * 2 + ((s16 & 3) >> 1);
 #pragma unroll
-        for (int b = 0; b < NVA; ++b)
-            vaddr[b] = vr * RB + (((4 * b + x) ^ Swz<D>::fv(vr)) << 4) + (s16 & 1) * 8;
+        for (int bb = 0; bb < NVA; ++bb)
+            vaddr[bb] = vr * RB + (((4 * bb + x) ^ Swz<D>::fv(vr)) << 4) + (s16 & 1) * 8;
     }
     // Issues the two transposing reads of a V fragment; the caller waits.
     auto vfrag_issue = [&](const char *vb, auto t_, auto db_) -> bf16x8 {
@@ -423,15 +427,21 @@ fa_fwd_kernel(Params p) {
         return __builtin_bit_cast(bf16x8, both);
     };
 
-    // ---- per-wave softmax state ---------------------------------------------------
-    f32x16 oacc[NDB];
+    // ---- per-wave softmax state (per query block) ---------------------------------
+    f32x16 oacc[QB][NDB];
 #pragma unroll
-    for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
-    float m_run = -INFINITY;  // reference max, scaled log2 units
-    float l_run = 0.0f;       // this lane's partial row sum
-    float m_use = 0.0f;       // subtrahend of the tile being exponentiated
-    float alpha = 1.0f;       // pending rescale of O for that tile
-    bool rescale_o = false;   // wave-uniform: some row's reference moved
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int i = 0; i < NDB; ++i) oacc[b][i] = f32x16{};
+    float m_run[QB], l_run[QB], m_use[QB], alpha[QB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+        m_run[b] = -INFINITY;  // reference max, scaled log2 units
+        l_run[b] = 0.0f;       // this lane's partial row sum
+        m_use[b] = 0.0f;       // subtrahend of the tile being exponentiated
+        alpha[b] = 1.0f;       // pending rescale of O for that tile
+    }
+    bool rescale_o = false;    // wave-uniform: some row's reference moved
     const float cs = p.cs;
 
     // -inf for tail keys (>= n) and, when causal, keys after the query.
@@ -439,93 +449,115 @@ fa_fwd_kernel(Params p) {
         const int kv0 = j * BC;
         return (CAUSAL && kv0 + BC - 1 > wrow0) || kv0 + BC > n;
     };
-    auto s_mask = [&](f32x16 (&s)[NKB], int j) {
+    auto s_mask = [&](f32x16 (&s)[QB][NKB], int j) {
         const int kv0 = j * BC;
 #pragma unroll
-        for (int kb2 = 0; kb2 < NKB; ++kb2) {
+        for (int b = 0; b < QB; ++b) {
+            const int qrow = wrow0 + 32 * b + c;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = kv0 + kb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-                const bool off = key >= n || (CAUSAL && key > qrow);
-                s[kb2][r] = off ? -INFINITY : s[kb2][r];
+            for (int kb2 = 0; kb2 < NKB; ++kb2) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kv0 + kb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+                    const bool off = key >= n || (CAUSAL && key > qrow);
+                    s[b][kb2][r] = off ? -INFINITY : s[b][kb2][r];
+                }
             }
         }
     };
-    // Reference max update from a tile's raw row max.
-    auto s_update = [&](float mx) {
-        mx = xhalf_max(mx);
-        const float mt = (mx == -INFINITY) ? -INFINITY : mx * cs;
-        float m_new;
-        bool grow;
-        if constexpr (RSM == FA_RESCALE_THRESHOLD) {
-            grow = mt > m_run + kTau;  // also true for the first finite tile
-            m_new = grow ? mt : m_run;
-        } else {
-            m_new = fmaxf(m_run, mt);
-            grow = m_new > m_run;
+    // Reference max update of every block from its tile's raw row max.
+    auto s_update = [&](float (&mx)[QB]) {
+        bool grow_any = false;
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+            const float x = xhalf_max(mx[b]);
+            const float mt = (x == -INFINITY) ? -INFINITY : x * cs;
+            float m_new;
+            bool grow;
+            if constexpr (RSM == FA_RESCALE_THRESHOLD) {
+                grow = mt > m_run[b] + kTau;  // also true for the first finite tile
+                m_new = grow ? mt : m_run[b];
+            } else {
+                m_new = fmaxf(m_run[b], mt);
+                grow = m_new > m_run[b];
+            }
+            m_use[b] = (m_new == -INFINITY) ? 0.0f : m_new;
+            alpha[b] = __builtin_amdgcn_exp2f(m_run[b] - m_use[b]);  // 1 if unchanged, 0 from -inf
+            l_run[b] *= alpha[b];
+            m_run[b] = m_new;
+            grow_any = grow_any || grow;
         }
-        m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-        alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 1 if unchanged, 0 from -inf
         if constexpr (RSM == FA_RESCALE_ALWAYS) {
             rescale_o = true;
         } else {
-            rescale_o = __ballot(grow) != 0;
+            rescale_o = __ballot(grow_any) != 0;
         }
-        l_run *= alpha;
-        m_run = m_new;
     };
-    auto s_rowmax = [&](const f32x16 (&s)[NKB]) {
-        float mx = -INFINITY;
+    auto s_rowmax = [&](const f32x16 (&s)[QB][NKB], float (&mx)[QB]) {
 #pragma unroll
-        for (int kb2 = 0; kb2 < NKB; ++kb2)
+        for (int b = 0; b < QB; ++b) {
+            mx[b] = -INFINITY;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb2][r]);
-        return mx;
+            for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx[b] = fmaxf(mx[b], s[b][kb2][r]);
+        }
     };
-    // S^T = K Q^T alone (prologue and pipeline edges).
-    auto s_mfma = [&](f32x16 (&s)[NKB], const char *kb) {
+    // S^T = K Q^T alone (prologue).
+    auto s_mfma = [&](f32x16 (&s)[QB][NKB], const char *kb) {
 #pragma unroll
-        for (int i = 0; i < NKB; ++i) s[i] = f32x16{};
+        for (int b = 0; b < QB; ++b)
+#pragma unroll
+            for (int i = 0; i < NKB; ++i) s[b][i] = f32x16{};
 #pragma unroll
         for (int m = 0; m < MS; ++m) {
-            const int kb2 = m / KK, kk = m % KK;
-            s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(kb, kk, kb2), qf[kk], s[kb2], 0, 0, 0);
+            const int kb2 = m % NKB, kk = m / NKB;
+            const bf16x8 kf = kfrag(kb, kk, kb2);
+#pragma unroll
+            for (int b = 0; b < QB; ++b)
+                s[b][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[b][kk], s[b][kb2], 0, 0, 0);
         }
     };
-    // P~ element e (0..NE-1) of S; e = kb2*16 + r, and pf[t] holds e = 8t..8t+7.
-    bf16x8 pf[NT16];
-    float pe[NE];
-    auto p_elem = [&](const f32x16 (&s)[NKB], int e) {
-        pe[e] = exp2_sel<EXPM>(__builtin_fmaf(s[e >> 4][e & 15], cs, -m_use), e);
+    // P~ element e (0..NE-1) of block b: e = kb2*16 + r, pf[b][t] holds e = 8t..8t+7.
+    bf16x8 pf[QB][NT16];
+    float pe[QB][NE];
+    auto p_elem = [&](const f32x16 (&s)[QB][NKB], int b, int e) {
+        pe[b][e] = exp2_sel<EXPM>(__builtin_fmaf(s[b][e >> 4][e & 15], cs, -m_use[b]), e);
     };
-    auto p_pack = [&](int t, float &rsum) {
+    auto p_pack = [&](int b, int t, float &rsum) {
         uint32_t pk[4];
 #pragma unroll
         for (int i = 0; i < 8; i += 2) {
-            rsum += pe[8 * t + i] + pe[8 * t + i + 1];
-            pk[i >> 1] = pack_bf16x2(pe[8 * t + i], pe[8 * t + i + 1]);
+            rsum += pe[b][8 * t + i] + pe[b][8 * t + i + 1];
+            pk[i >> 1] = pack_bf16x2(pe[b][8 * t + i], pe[b][8 * t + i + 1]);
         }
         u32x4 pv = {pk[0], pk[1], pk[2], pk[3]};
-        pf[t] = __builtin_bit_cast(bf16x8, pv);
+        pf[b][t] = __builtin_bit_cast(bf16x8, pv);
     };
-    auto p_exp = [&](const f32x16 (&s)[NKB]) {
-        float rsum = 0.0f;
+    auto p_exp = [&](const f32x16 (&s)[QB][NKB]) {
 #pragma unroll
-        for (int e = 0; e < NE; ++e) {
-            p_elem(s, e);
-            if ((e & 7) == 7) p_pack(e >> 3, rsum);
+        for (int b = 0; b < QB; ++b) {
+            float rsum = 0.0f;
+#pragma unroll
+            for (int e = 0; e < NE; ++e) {
+                p_elem(s, b, e);
+                if ((e & 7) == 7) p_pack(b, e >> 3, rsum);
+            }
+            l_run[b] += rsum;
         }
-        l_run += rsum;
     };
-    auto o_rescale = [&](float a) {
+    auto o_rescale = [&]() {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+        for (int b = 0; b < QB; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][r] *= a;
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[b][db][r] *= alpha[b];
     };
-    // PV product: O^T += V^T P^T, MFMA order t-major (all d blocks of key
-    // chunk t, then chunk t+1), V fragments read two MFMAs ahead.  `work(m)`
-    // is VALU work placed after MFMA m; it may produce pf[t] for a later t.
+    // PV product: O^T += V^T P^T, step order t-major (all d blocks of key chunk
+    // t, then chunk t+1), V fragments read two steps ahead, QB MFMAs per step.
+    // `work(m)` is VALU work placed after step m; it may produce pf[.][t] for a
+    // later t.
     auto pv_run = [&](const char *vb, auto &&work) {
         bf16x8 vf[MS];
         static_for<0, (MS < 2 ? MS : 2)>([&](auto m) {
@@ -536,7 +568,9 @@ fa_fwd_kernel(Params p) {
             constexpr int t = m / NDB, db = m % NDB;
             if constexpr (m + 1 < MS) lgkm_wait<2>(vf[m]);
             else lgkm_wait<0>(vf[m]);
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[m], pf[t], oacc[db], 0, 0, 0);
+#pragma unroll
+            for (int b = 0; b < QB; ++b)
+                oacc[b][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[m], pf[b][t], oacc[b][db], 0, 0, 0);
             if constexpr (m + 2 < MS)
                 vf[m + 2] = vfrag_issue(vb, std::integral_constant<int, (m + 2) / NDB>{},
                                         std::integral_constant<int, (m + 2) % NDB>{});
@@ -546,82 +580,96 @@ fa_fwd_kernel(Params p) {
     auto pv_mfma = [&](const char *vb) { pv_run(vb, [](auto) {}); };
 
     // The exponentials of S_j are split between the two phases: [A] does key
-    // chunks 0 .. NT16/2-1 (one element per S MFMA), [B] the rest, chunk
-    // NT16/2 + i during PV MFMAs i*NDB .. (i+1)*NDB-1, i.e. before the first
-    // MFMA that needs it.  [B] then takes the row max of S_{j+1}.  The
-    // sched_group_barrier sequences spread the VALU work evenly between the
-    // MFMAs (a wave issues in order; a burst of exponentials between two MFMAs
-    // would hold back the second).
-    constexpr int HALF = NE / 2;          // elements per phase
-    // [A]: S MFMA m takes elements [m*HALF/MS, (m+1)*HALF/MS)
+    // chunks 0 .. NT16/2-1 of every block, [B] the rest, chunk NT16/2 + i during
+    // PV steps i*NDB .. (i+1)*NDB-1, i.e. before the first step that needs it.
+    // [B] then takes the row max of S_{j+1}.  The sched_group_barrier sequences
+    // spread the VALU work evenly between the MFMAs (a wave issues in order; a
+    // burst of exponentials between two MFMAs would hold back the second), and
+    // anchor() keeps [A]'s exponentials inside [A].
+    constexpr int HALF = NE / 2;          // elements per block per phase
+    constexpr int AE = QB * HALF;         // [A] elements (all blocks)
+    float rsum_a[QB];
 
-    // [A]: S_{j+1} MFMAs interleaved with the first half of the exponentials
-    // of S_j.
-    float rsum_a = 0.0f;
-    auto phase_a = [&](f32x16 (&nxt)[NKB], const f32x16 (&cur)[NKB], const char *kb) {
+    // [A]: S_{j+1} MFMAs interleaved with the first half of the exponentials of S_j.
+    auto phase_a = [&](f32x16 (&nxt)[QB][NKB], const f32x16 (&cur)[QB][NKB], const char *kb) {
 #pragma unroll
-        for (int i = 0; i < NKB; ++i) nxt[i] = f32x16{};
-        float rsum = 0.0f;
+        for (int b = 0; b < QB; ++b) {
+            rsum_a[b] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NKB; ++i) nxt[b][i] = f32x16{};
+        }
         bf16x8 kf[3];
-        // MFMA order alternates the NKB accumulator chains
+        // step order alternates the NKB accumulator chains
         kf[0] = kfrag(kb, 0, 0);
         if constexpr (MS > 1) kf[1] = kfrag(kb, 1 / NKB, 1 % NKB);
         static_for<0, MS>([&](auto m) {
             constexpr int kb2 = m % NKB, kk = m / NKB;
             if constexpr (m + 2 < MS) kf[(m + 2) % 3] = kfrag(kb, (m + 2) / NKB, (m + 2) % NKB);
-            nxt[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[m % 3], qf[kk], nxt[kb2], 0, 0, 0);
 #pragma unroll
-            for (int e = m * HALF / MS; e < (m + 1) * HALF / MS; ++e) {
-                p_elem(cur, e);
-                anchor(pe[e]);
-                if ((e & 7) == 7) p_pack(e >> 3, rsum);
+            for (int b = 0; b < QB; ++b)
+                nxt[b][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[m % 3], qf[b][kk], nxt[b][kb2], 0, 0, 0);
+            // elements [m*AE/MS, (m+1)*AE/MS) of the list (b, e), b-major
+#pragma unroll
+            for (int x = m * AE / MS; x < (m + 1) * AE / MS; ++x) {
+                const int b = x / HALF, e = x % HALF;
+                p_elem(cur, b, e);
+                anchor(pe[b][e]);
+                if ((e & 7) == 7) p_pack(b, e >> 3, rsum_a[b]);
             }
         });
-        anchor(rsum);
+#pragma unroll
+        for (int b = 0; b < QB; ++b) anchor(rsum_a[b]);
         __builtin_amdgcn_sched_group_barrier(0x100, MS > 1 ? 2 : 1, 0);  // first K fragments
         static_for<0, MS>([&](auto m) {
-            constexpr int ne = (m + 1) * HALF / MS - m * HALF / MS;  // elements of this step
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            constexpr int ne = (m + 1) * AE / MS - m * AE / MS;  // elements of this step
+            __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);  // MFMA
             if constexpr (m + 2 < MS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
             if constexpr (ne > 0) __builtin_amdgcn_sched_group_barrier(0x402, 3 * ne + (ne + 1) / 2, 0);
         });
-        rsum_a = rsum;
     };
     // [B]: PV MFMAs interleaved with the second half of the exponentials of
     // S_j and the row max of S_{j+1}.
-    auto phase_b = [&](const f32x16 (&nxt)[NKB], const f32x16 (&cur)[NKB], const char *vb) {
-        constexpr int EB = 8 / NDB;                 // elements per MFMA, first half of [B]
-        constexpr int MB = NE / (MS - MS / 2);      // max elements per MFMA, second half
-        static_assert(8 % NDB == 0 && NE % (MS - MS / 2) == 0, "element split");
-        float rsum = rsum_a;
-        float mx = -INFINITY;
+    auto phase_b = [&](const f32x16 (&nxt)[QB][NKB], const f32x16 (&cur)[QB][NKB], const char *vb,
+                       float (&mx)[QB]) {
+        constexpr int EB = QB * 8 / NDB;                // exp elements per step, first half of [B]
+        constexpr int MB = QB * NE / (MS - MS / 2);     // max elements per step, second half
+        static_assert((QB * 8) % NDB == 0 && (QB * NE) % (MS - MS / 2) == 0, "element split");
+        float rsum[QB];
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+            rsum[b] = rsum_a[b];
+            mx[b] = -INFINITY;
+        }
         pv_run(vb, [&](auto m) {
             if constexpr (m < MS / 2) {
+                // chunk NT16/2 + m / NDB of every block: elements (b, 8 t + i)
 #pragma unroll
-                for (int i = 0; i < EB; ++i) {
-                    const int e = HALF + m * EB + i;
-                    p_elem(cur, e);
-                    if ((e & 7) == 7) p_pack(e >> 3, rsum);
+                for (int x = m * EB; x < (m + 1) * EB; ++x) {
+                    const int t = NT16 / 2 + x / (QB * 8);
+                    const int b = (x / 8) % QB, i = x % 8;
+                    const int e = 8 * t + i;
+                    p_elem(cur, b, e);
+                    if (i == 7) p_pack(b, t, rsum[b]);
                 }
             } else {
 #pragma unroll
-                for (int i = 0; i < MB; ++i) {
-                    const int e = (m - MS / 2) * MB + i;
-                    mx = fmaxf(mx, nxt[e >> 4][e & 15]);
+                for (int x = (m - MS / 2) * MB; x < (m - MS / 2 + 1) * MB; ++x) {
+                    const int b = x / NE, e = x % NE;
+                    mx[b] = fmaxf(mx[b], nxt[b][e >> 4][e & 15]);
                 }
             }
         });
         static_for<0, MS>([&](auto m) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);  // MFMA
             if constexpr (m < MS / 2) __builtin_amdgcn_sched_group_barrier(0x402, 3 * EB + (EB + 1) / 2, 0);
             else __builtin_amdgcn_sched_group_barrier(0x402, (MB + 1) / 2, 0);
         });
-        l_run += rsum;
-        return mx;
+#pragma unroll
+        for (int b = 0; b < QB; ++b) l_run[b] += rsum[b];
     };
 
     // ---- prologue: K_0, V_0, K_1 into LDS; S_0 and its row max ------------------
-    f32x16 sa[NKB], sb[NKB];
+    f32x16 sa[QB][NKB], sb[QB][NKB];
     dma_k(k_lds0, 0);
     dma_v(v_lds0, 0);
     if (nkv > 1) dma_k(k_lds1, 1);
@@ -630,7 +678,9 @@ fa_fwd_kernel(Params p) {
     if (nkv_w > 0) {
         s_mfma(sa, k_lds0);
         if (need_mask(0)) s_mask(sa, 0);
-        s_update(s_rowmax(sa));
+        float mx[QB];
+        s_rowmax(sa, mx);
+        s_update(mx);
     }
     __syncthreads();  // K tile 0 is reloaded at the start of iteration 0
 
@@ -648,23 +698,25 @@ fa_fwd_kernel(Params p) {
     // PAR = j & 1 selects the LDS tiles statically.  MASK: tile j+1 needs the
     // tail/causal mask (kept out of the hot loop so that nothing separates
     // phase [A] from phase [B]).
-    auto full_step = [&](auto par, auto mask, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB], int j) {
+    auto full_step = [&](auto par, auto mask, f32x16 (&cur)[QB][NKB], f32x16 (&nxt)[QB][NKB], int j) {
         constexpr int PAR = decltype(par)::value;
         issue_loads(j, (PAR ? k_lds1 : k_lds0), (PAR ? v_lds0 : v_lds1));
-        if (rescale_o) o_rescale(alpha);
+        if (rescale_o) o_rescale();
         __builtin_amdgcn_sched_barrier(0);
         phase_a(nxt, cur, (PAR ? k_lds0 : k_lds1));  // K_{j+1}
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (decltype(mask)::value) s_mask(nxt, j + 1);
-        s_update(phase_b(nxt, cur, (PAR ? v_lds1 : v_lds0)));  // V_j
+        float mx[QB];
+        phase_b(nxt, cur, (PAR ? v_lds1 : v_lds0), mx);  // V_j
+        s_update(mx);
         __builtin_amdgcn_sched_barrier(0);
         end_iteration();
     };
     // The wave's last tile: no next S.
-    auto drain_step = [&](const f32x16 (&cur)[NKB], int j) {
+    auto drain_step = [&](const f32x16 (&cur)[QB][NKB], int j) {
         const int par = j & 1;
         issue_loads(j, (par ? k_lds1 : k_lds0), (par ? v_lds0 : v_lds1));
-        if (rescale_o) o_rescale(alpha);
+        if (rescale_o) o_rescale();
         p_exp(cur);
         pv_mfma((par ? v_lds1 : v_lds0));
         end_iteration();
@@ -705,26 +757,27 @@ fa_fwd_kernel(Params p) {
     }
 
     // ---- epilogue: O / l, LSE = (m + log2 l) ln 2 ----------------------------
-    const float l = xhalf_sum(l_run);
-    {
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+        const int rowb = wrow0 + 32 * b;
+        const float l = xhalf_sum(l_run[b]);
         // rows >= n fall outside the buffer and are dropped
         const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-        const auto ors = make_rsrc(p.o + base + wrow0 * rs, (long long)(n - wrow0) * rs * 2);
-        const int voff = c * static_cast<int>(rs) * 2;
+        const auto ors = make_rsrc(p.o + base + rowb * rs, (long long)(n - rowb) * rs * 2);
+        const int voff_o = c * static_cast<int>(rs) * 2;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int col = db * 32 + g4 * 8 + hh * 4;
-                u32x2 v2 = {pack_bf16x2(oacc[db][g4 * 4 + 0] * inv, oacc[db][g4 * 4 + 1] * inv),
-                            pack_bf16x2(oacc[db][g4 * 4 + 2] * inv, oacc[db][g4 * 4 + 3] * inv)};
-                __builtin_amdgcn_raw_buffer_store_b64(v2, ors, voff + col * 2, 0, 0);
+                u32x2 v2 = {pack_bf16x2(oacc[b][db][g4 * 4 + 0] * inv, oacc[b][db][g4 * 4 + 1] * inv),
+                            pack_bf16x2(oacc[b][db][g4 * 4 + 2] * inv, oacc[b][db][g4 * 4 + 3] * inv)};
+                __builtin_amdgcn_raw_buffer_store_b64(v2, ors, voff_o + col * 2, 0, 0);
             }
         }
-    }
-    if (qrow < n) {
-        if (hh == 0) {
-            const float lse = l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+        const int qrow = rowb + c;
+        if (qrow < n && hh == 0) {
+            const float lse = l > 0.0f ? (m_run[b] + log2f(l)) * kLn2 : -INFINITY;
             long long li;
             if constexpr (VARLEN) {
                 li = static_cast<long long>(w.h) * p.N + w.t0 + qrow;
@@ -736,14 +789,13 @@ fa_fwd_kernel(Params p) {
     }
 }
 
-
 template <int D, bool CAUSAL, bool VARLEN, int EXPM>
 KernelFn select_rsm(int rsm) {
-    constexpr int BC = kTileKeys, NW = kWorkgroupWaves;
+    constexpr int BC = kTileKeys, NW = kWorkgroupWaves, QB = Geometry<D>::kBlocks;
     switch (rsm) {
-        case FA_RESCALE_ALWAYS: return fa_fwd_kernel<D, BC, NW, CAUSAL, VARLEN, EXPM, FA_RESCALE_ALWAYS>;
-        case FA_RESCALE_STRICT: return fa_fwd_kernel<D, BC, NW, CAUSAL, VARLEN, EXPM, FA_RESCALE_STRICT>;
-        default: return fa_fwd_kernel<D, BC, NW, CAUSAL, VARLEN, EXPM, FA_RESCALE_THRESHOLD>;
+        case FA_RESCALE_ALWAYS: return fa_fwd_kernel<D, BC, NW, QB, CAUSAL, VARLEN, EXPM, FA_RESCALE_ALWAYS>;
+        case FA_RESCALE_STRICT: return fa_fwd_kernel<D, BC, NW, QB, CAUSAL, VARLEN, EXPM, FA_RESCALE_STRICT>;
+        default: return fa_fwd_kernel<D, BC, NW, QB, CAUSAL, VARLEN, EXPM, FA_RESCALE_THRESHOLD>;
     }
 }
 
