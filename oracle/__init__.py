@@ -64,6 +64,12 @@ def load_library(path: str | None = None):
     fn.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4 + [
         ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    fr = lib.oracle_attention_rows_range
+    fr.restype = ctypes.c_int
+    fr.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int]
     if path is None:
         _lib = lib
     return lib
@@ -95,7 +101,7 @@ def all_rows(B: int, H: int, lengths) -> np.ndarray:
 
 
 def attention(q, k, v, *, scale: float, causal: bool, cu_seqlens=None,
-              rows=None, nthreads: int | None = None, lib=None):
+              rows=None, nthreads: int | None = None, lib=None, key_range=None):
     """Exact attention forward in fp64.
 
     q, k, v    uint16 arrays: ``[B, N, H, d]`` (dense) or ``[T, H, d]``
@@ -103,6 +109,9 @@ def attention(q, k, v, *, scale: float, causal: bool, cu_seqlens=None,
     scale      the fp32 softmax scale (widened to double as given).
     rows       None for every row, or an ``(n, 3)`` int array of
                ``(b, h, i)`` triples.
+    key_range  None for every visible key, or ``(lo, hi)``: only keys
+               ``lo <= j < hi`` (indices within the sequence) take part.  A
+               row with no key left gets ``O = 0`` and ``LSE = -inf``.
     Returns ``(o, lse)`` as float64: full layouts (``o`` shaped like ``q``,
     ``lse`` ``[B, H, N]`` or ``[H, T]``) when ``rows`` is None, else
     ``o [n, d]`` and ``lse [n]``.
@@ -139,13 +148,18 @@ def attention(q, k, v, *, scale: float, causal: bool, cu_seqlens=None,
     o = np.zeros((n, d), dtype=np.float64)
     lse = np.zeros((n,), dtype=np.float64)
     if n > 0:
-        rc = lib.oracle_attention_rows(
-            _ptr(q), _ptr(k), _ptr(v), B, H, max(nmax, 1), d,
-            ctypes.c_float(scale), int(bool(causal)),
-            _ptr(cu) if cu is not None else None, n, _ptr(rows), _ptr(o),
-            _ptr(lse), int(nthreads or default_threads()))
+        common = (_ptr(q), _ptr(k), _ptr(v), B, H, max(nmax, 1), d,
+                  ctypes.c_float(scale), int(bool(causal)),
+                  _ptr(cu) if cu is not None else None, n, _ptr(rows))
+        if key_range is None:
+            rc = lib.oracle_attention_rows(*common, _ptr(o), _ptr(lse),
+                                           int(nthreads or default_threads()))
+        else:
+            lo, hi = (int(x) for x in key_range)
+            rc = lib.oracle_attention_rows_range(*common, lo, hi, _ptr(o), _ptr(lse),
+                                                 int(nthreads or default_threads()))
         if rc != 0:
-            raise RuntimeError(f"oracle_attention_rows failed with code {rc}")
+            raise RuntimeError(f"oracle attention rows failed with code {rc}")
     if not full:
         return o, lse
     # scatter into the tensor layouts
@@ -160,3 +174,31 @@ def attention(q, k, v, *, scale: float, causal: bool, cu_seqlens=None,
         o_full[tok, rows[:, 1], :] = o
         lse_full[rows[:, 1], tok] = lse
     return o_full, lse_full
+
+
+def merge(o_parts, lse_parts):
+    """Combine attention results over disjoint key ranges into the result
+    over their union, in fp64.
+
+    ``o_parts``: ``[S, ...rows..., d]`` normalised partial outputs;
+    ``lse_parts``: ``[S, ...rows...]`` their log-sum-exps (``-inf`` for a
+    range with no key).  Each part is a softmax over its own keys, so with
+    ``LSE = ln sum_s exp(LSE_s)`` the union's weights are the parts' weights
+    times ``exp(LSE_s - LSE)``: ``O = sum_s exp(LSE_s - LSE) O_s``.  This is
+    the rescaling the FlashAttention-2 section of the FlashAttention 1-4 post
+    applies when the key/value sequence is split.  Returns ``(o, lse)``.
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    if o_parts.shape[:-1] != lse_parts.shape:
+        raise ValueError("o_parts must be lse_parts' shape plus a trailing d")
+    m = np.max(lse_parts, axis=0)
+    safe = np.where(np.isfinite(m), m, 0.0)          # no key anywhere: keep -inf
+    w = np.exp(lse_parts - safe[None])                 # exp(-inf) = 0 for empty parts
+    tot = np.sum(w, axis=0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        lse = safe + np.log(tot)
+        o = np.sum(w[..., None] * o_parts, axis=0) / tot[..., None]
+    o = np.where((tot > 0)[..., None], o, 0.0)
+    lse = np.where(tot > 0, lse, -np.inf)
+    return o, lse

@@ -28,6 +28,14 @@
  *   - dense tensors are [B, N, H, d]; packed variable-length tensors are
  *     [T, H, d] with sequence b spanning tokens cu_seqlens[b]..cu_seqlens[b+1].
  *
+ * A key range [kv_lo, kv_hi) may further restrict the visible keys.  The
+ * result is then the attention of each row over that part of the sequence
+ * alone: the partial output and log-sum-exp that a split of the key/value
+ * sequence produces (the "parallel along the sequence" discussion of the
+ * FlashAttention 1-4 post, FlashAttention-2 section).  A row that sees no
+ * key in the range gets O = 0 and LSE = -inf, the neutral element of the
+ * merge that combines such partials.
+ *
  * The S row is materialised in full, exactly as the naive method of the
  * pages does (and as the fused kernel avoids); memory stays bounded because
  * only one row per thread exists at a time.
@@ -51,6 +59,7 @@ static double widen_bf16(uint16_t bits)
 struct job {
     const uint16_t *q, *k, *v;
     int B, H, N, d, causal;
+    int kv_lo, kv_hi;           /* key range, intersected with the visible keys */
     double scale;
     const int32_t *cu;          /* NULL for dense */
     const int64_t *rows;        /* triples (b, h, i) */
@@ -80,12 +89,21 @@ static void one_row(const struct job *jb, int64_t r, double *s)
     int n;
     seq_span(jb, b, &t0, &n);
 
-    /* visible keys: j < n, and j <= i when causal */
+    /* visible keys: j < n, and j <= i when causal; then [kv_lo, kv_hi) */
     const int nvis = jb->causal ? i + 1 : n;
+    const int lo = jb->kv_lo > 0 ? jb->kv_lo : 0;
+    const int hi = jb->kv_hi < nvis ? jb->kv_hi : nvis;
     const uint16_t *qi = jb->q + ((t0 + i) * H + h) * (int64_t)d;
+    double *oi = jb->o + r * (int64_t)d;
+    if (hi <= lo) {
+        /* no key: empty sum, O = 0 and LSE = ln 0 */
+        for (int x = 0; x < d; ++x) oi[x] = 0.0;
+        jb->lse[r] = -INFINITY;
+        return;
+    }
 
     /* S_ij = scale * (q_i . k_j) */
-    for (int j = 0; j < nvis; ++j) {
+    for (int j = lo; j < hi; ++j) {
         const uint16_t *kj = jb->k + ((t0 + j) * H + h) * (int64_t)d;
         double dot = 0.0;
         for (int x = 0; x < d; ++x)
@@ -95,18 +113,17 @@ static void one_row(const struct job *jb, int64_t r, double *s)
 
     /* m = row max; e_j = exp(S_ij - m); l = sum e_j */
     double m = -INFINITY;
-    for (int j = 0; j < nvis; ++j)
+    for (int j = lo; j < hi; ++j)
         if (s[j] > m) m = s[j];
     double l = 0.0;
-    for (int j = 0; j < nvis; ++j) {
+    for (int j = lo; j < hi; ++j) {
         s[j] = exp(s[j] - m);
         l += s[j];
     }
 
     /* O_i = sum_j (e_j / l) v_j */
-    double *oi = jb->o + r * (int64_t)d;
     for (int x = 0; x < d; ++x) oi[x] = 0.0;
-    for (int j = 0; j < nvis; ++j) {
+    for (int j = lo; j < hi; ++j) {
         const double p = s[j] / l;
         const uint16_t *vj = jb->v + ((t0 + j) * H + h) * (int64_t)d;
         for (int x = 0; x < d; ++x)
@@ -130,22 +147,24 @@ static void *worker(void *arg)
 }
 
 /*
- * Attention output for a list of rows.
+ * Attention output for a list of rows, over the keys j in [kv_lo, kv_hi)
+ * that the row sees.
  *   q, k, v   host bf16 bit patterns, [B, N, H, d] (cu_seqlens == NULL) or
  *             [T, H, d] (cu_seqlens != NULL, T = cu_seqlens[B]).
  *   N         sequence length (dense) or the longest sequence (packed); it
  *             sizes the per-thread score row.
  *   rows      n_rows triples (b, h, i): sequence, head, query index within
  *             the sequence.
+ *   kv_lo, kv_hi  key range (indices within the sequence); 0 and N for all.
  *   o_out     n_rows x d doubles; lse_out n_rows doubles.
  *   nthreads  worker threads (>= 1).
  * Returns 0, or a non-zero code for a bad argument or row.
  */
-int oracle_attention_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                          int B, int H, int N, int d, float scale, int causal,
-                          const int32_t *cu_seqlens, int64_t n_rows,
-                          const int64_t *rows, double *o_out, double *lse_out,
-                          int nthreads)
+int oracle_attention_rows_range(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                int B, int H, int N, int d, float scale, int causal,
+                                const int32_t *cu_seqlens, int64_t n_rows,
+                                const int64_t *rows, int kv_lo, int kv_hi,
+                                double *o_out, double *lse_out, int nthreads)
 {
     if (!q || !k || !v || !rows || !o_out || !lse_out) return ORACLE_ERR_ARG;
     if (B <= 0 || H <= 0 || N <= 0 || d <= 0 || n_rows < 0 || nthreads <= 0)
@@ -155,6 +174,7 @@ int oracle_attention_rows(const uint16_t *q, const uint16_t *k, const uint16_t *
     memset(&base, 0, sizeof base);
     base.q = q; base.k = k; base.v = v;
     base.B = B; base.H = H; base.N = N; base.d = d; base.causal = causal != 0;
+    base.kv_lo = kv_lo; base.kv_hi = kv_hi;
     base.scale = (double)scale;
     base.cu = cu_seqlens;
     base.rows = rows;
@@ -197,4 +217,15 @@ int oracle_attention_rows(const uint16_t *q, const uint16_t *k, const uint16_t *
     free(tid);
     free(joinable);
     return rc;
+}
+
+/* Attention output for a list of rows over every visible key (see above). */
+int oracle_attention_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                          int B, int H, int N, int d, float scale, int causal,
+                          const int32_t *cu_seqlens, int64_t n_rows,
+                          const int64_t *rows, double *o_out, double *lse_out,
+                          int nthreads)
+{
+    return oracle_attention_rows_range(q, k, v, B, H, N, d, scale, causal, cu_seqlens,
+                                       n_rows, rows, 0, N, o_out, lse_out, nthreads);
 }

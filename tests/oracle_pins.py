@@ -23,6 +23,7 @@ import os
 import numpy as np
 
 from exact_attention_107_amd.workloads import bf16_bits, bf16_to_f32
+from oracle import merge as oracle_merge
 from oracle.online import online_attention
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_worked.json")
@@ -278,9 +279,76 @@ def pin_large_logits(attn):
         _close(lse, rl, 1e-9, "large-logit LSE")
 
 
+def pin_key_range_subsequence(attn):
+    """Attention over keys [lo, hi) equals scipy's softmax over those keys
+    alone (with the causal mask in sequence indices)."""
+    from scipy.special import logsumexp, softmax
+    rng = np.random.Generator(np.random.PCG64(24))
+    B, N, H, d = 1, 23, 2, 8
+    q, k, v = (_rand_bits(rng, (B, N, H, d)) for _ in range(3))
+    Q, K, V = _f64(q), _f64(k), _f64(v)
+    sc = float(np.float32(0.4))
+    for causal in (False, True):
+        for lo, hi in ((0, 23), (5, 17), (11, 12), (20, 99)):
+            o, lse = attn(q, k, v, scale=0.4, causal=causal, key_range=(lo, hi))
+            hi_c = min(hi, N)
+            for h in range(H):
+                S = (Q[0, :, h, :] @ K[0, lo:hi_c, h, :].T) * sc
+                if causal:
+                    S = np.where(np.arange(lo, hi_c)[None, :] <= np.arange(N)[:, None], S, -np.inf)
+                seen = np.isfinite(S).any(axis=1)
+                Ssafe = np.where(seen[:, None], S, 0.0)
+                ro = np.where(seen[:, None], softmax(Ssafe, axis=1) @ V[0, lo:hi_c, h, :], 0.0)
+                rl = np.where(seen, logsumexp(Ssafe, axis=1), -np.inf)
+                _close(o[0, :, h, :], ro, 1e-12, f"range [{lo},{hi}) causal={causal} O")
+                assert np.array_equal(np.isinf(lse[0, h]), ~seen), "empty rows must give LSE = -inf"
+                _close(lse[0, h][seen], rl[seen], 1e-12, f"range [{lo},{hi}) LSE")
+
+
+def pin_key_range_single_key(attn):
+    """A range holding one visible key: O = V_j, LSE = scale q_i . k_j."""
+    rng = np.random.Generator(np.random.PCG64(25))
+    B, N, H, d = 2, 9, 1, 16
+    q, k, v = (_rand_bits(rng, (B, N, H, d)) for _ in range(3))
+    Q, K, V = _f64(q), _f64(k), _f64(v)
+    sc = float(np.float32(0.25))
+    for j in (0, 4, 8):
+        o, lse = attn(q, k, v, scale=0.25, causal=False, key_range=(j, j + 1))
+        _close(o[:, :, 0, :], np.broadcast_to(V[:, j:j + 1, 0, :], (B, N, d)), 0.0, "one-key O")
+        _close(lse[:, 0, :], sc * np.einsum("bnd,bd->bn", Q[:, :, 0, :], K[:, j, 0, :]), 1e-13,
+               "one-key LSE")
+
+
+def pin_key_range_partition_merge(attn):
+    """Partials over a partition of the keys merge into the full result: the
+    softmax over a union is the LSE-weighted mix of the parts' softmaxes."""
+    rng = np.random.Generator(np.random.PCG64(26))
+    B, N, H, d = 2, 29, 2, 8
+    q, k, v = (_rand_bits(rng, (B, N, H, d), 2.0) for _ in range(3))
+    for causal in (False, True):
+        full_o, full_l = attn(q, k, v, scale=0.35, causal=causal)
+        for cuts in ((0, 29), (0, 7, 29), (0, 3, 16, 17, 29), (0, 10, 20, 40)):
+            parts = [attn(q, k, v, scale=0.35, causal=causal, key_range=(a, b))
+                     for a, b in zip(cuts[:-1], cuts[1:])]
+            # lse [B, H, N] -> [B, N, H], the leading shape of o [B, N, H, d]
+            o_m, l_m = oracle_merge(np.stack([p[0] for p in parts]),
+                                    np.stack([p[1].transpose(0, 2, 1) for p in parts]))
+            _close(o_m, full_o, 1e-12, f"merge {cuts} causal={causal} O")
+            _close(l_m.transpose(0, 2, 1), full_l, 1e-12, f"merge {cuts} causal={causal} LSE")
+        # an empty part changes nothing
+        o1, l1 = attn(q, k, v, scale=0.35, causal=causal, key_range=(0, N))
+        oe, le = attn(q, k, v, scale=0.35, causal=causal, key_range=(N, N + 5))
+        assert np.all(oe == 0.0) and np.all(np.isneginf(le))
+        o_m, l_m = oracle_merge(np.stack([oe, o1]),
+                                np.stack([le.transpose(0, 2, 1), l1.transpose(0, 2, 1)]))
+        _close(o_m, full_o, 1e-15, "merge with an empty part O")
+        _close(l_m.transpose(0, 2, 1), full_l, 1e-15, "merge with an empty part LSE")
+
+
 ALL_PINS = [
     pin_scipy_dense, pin_torch_sdpa, pin_online_recurrence, pin_hand_worked,
     pin_uniform_scores, pin_constant_v, pin_causal_first_row_and_single_key,
     pin_two_keys_logistic, pin_permutation_equivariance, pin_causal_future_independence,
     pin_shift_invariance, pin_packed_equals_dense, pin_row_subset, pin_large_logits,
+    pin_key_range_subsequence, pin_key_range_single_key, pin_key_range_partition_merge,
 ]

@@ -8,6 +8,7 @@ import os
 import shutil
 import subprocess
 
+import numpy as np
 import pytest
 
 import oracle
@@ -37,6 +38,11 @@ MUTANTS = {
     "dot_drops_last_dim": ("for (int x = 0; x < d; ++x)\n            dot +=",
                            "for (int x = 0; x < d - 1; ++x)\n            dot +="),
     "packed_ignores_offset": ("*start = jb->cu[b];", "*start = 0;"),
+    "range_high_inclusive": ("const int hi = jb->kv_hi < nvis ? jb->kv_hi : nvis;",
+                             "const int hi = jb->kv_hi + 1 < nvis ? jb->kv_hi + 1 : nvis;"),
+    "range_ignores_low": ("const int lo = jb->kv_lo > 0 ? jb->kv_lo : 0;", "const int lo = 0;"),
+    "range_ignores_causal": ("const int hi = jb->kv_hi < nvis ? jb->kv_hi : nvis;",
+                             "const int hi = jb->kv_hi < jb->N ? jb->kv_hi : jb->N;"),
 }
 
 
@@ -66,3 +72,23 @@ def test_mutant_is_caught(name, builddir):
         except (AssertionError, RuntimeError, FloatingPointError, ValueError):
             caught.append(pin.__name__)
     assert caught, f"mutant {name} passed every pin"
+
+
+MERGE_MUTANTS = {
+    # plain mean of the parts: ignores how much mass each part holds
+    "merge_unweighted": lambda o, l: (np.mean(o, axis=0), np.log(np.sum(np.exp(l), axis=0))),
+    # weights exp(LSE_s) without normalising by their sum
+    "merge_unnormalised": lambda o, l: (np.sum(np.exp(l)[..., None] * o, axis=0),
+                                        np.log(np.sum(np.exp(l), axis=0))),
+    # log of the mean instead of the sum
+    "merge_lse_mean": lambda o, l: (oracle.merge(o, l)[0], np.log(np.mean(np.exp(l), axis=0))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MERGE_MUTANTS))
+def test_merge_mutant_is_caught(name, monkeypatch, oracle_lib):
+    import oracle_pins
+    monkeypatch.setattr(oracle_pins, "oracle_merge", MERGE_MUTANTS[name])
+    attn = functools.partial(oracle.attention, lib=oracle_lib)
+    with np.errstate(all="ignore"), pytest.raises(AssertionError):
+        oracle_pins.pin_key_range_partition_merge(attn)
