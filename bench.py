@@ -26,7 +26,8 @@ PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense BF16 flop/clk/CU (the
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fa_fwd_wide.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_107_amd", "csrc", f)
                   for f in ("fa_kernel.hpp", "fa_internal.h", "fa_kernels_d64.hip",
-                            "fa_kernels_d128.hip", "fa_kernels_d256.hip", "fa_api.hip")] + \
+                            "fa_kernels_d128.hip", "fa_kernels_d256.hip", "fa_merge.hip",
+                            "fa_api.hip")] + \
                  [os.path.join(ROOT, "exact_attention_107_amd", "build.py")]
 
 
@@ -106,6 +107,54 @@ def cpu_baseline(inp, target_s: float):
                   f"({f / total * 100:.3f}% of its credited flops), fp64, {dt:.1f} s wall",
         "seconds": dt, "full_run_seconds_extrapolated": dt * total / f,
     }
+
+
+def split_kv_runs(torch, fa):
+    """Few-head runs: fa_fwd alone vs fa_fwd_splitkv at the library's suggested
+    split count (both kernels inside the timed launch), and the merge kernel
+    alone against the HBM roofline."""
+    from exact_attention_107_amd.workloads import RUNS, flops, make_inputs
+    res = {}
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for name in ("few_heads", "few_heads_causal"):
+        r = RUNS[name]
+        log(f"[bench] split-KV run {name}")
+        ri = make_inputs(r)
+        q, k, v = (to_dev(ri[x], torch) for x in ("q", "k", "v"))
+        o = torch.empty_like(q)
+        lse = torch.empty((r.B, r.H, r.N), dtype=torch.float32, device="cuda")
+        S = fa.num_splits(r.B, r.H, r.N, r.d, r.causal, cus)
+        op = torch.empty((S, r.B, r.N, r.H, r.d), dtype=torch.float32, device="cuda")
+        lp = torch.empty((S, r.B, r.H, r.N), dtype=torch.float32, device="cuda")
+        f = flops(ri["lengths"], r.H, r.d, r.causal)
+
+        def plain():
+            fa.fwd(q, k, v, causal=r.causal, scale=ri["scale"], out=o, lse=lse)
+
+        def split():
+            fa.fwd_splitkv(q, k, v, causal=r.causal, scale=ri["scale"], splits=S, out=o, lse=lse,
+                           o_part=op, lse_part=lp)
+
+        def merge():
+            fa.merge(op, lp, out=o, lse=lse)
+
+        _, ms_plain, _, _ = time_launches(plain, 20, 3, torch)
+        _, ms_split, _, _ = time_launches(split, 20, 3, torch)
+        _, ms_merge, _, _ = time_launches(merge, 20, 3, torch)
+        rows = r.B * r.N * r.H
+        merge_bytes = rows * (S * (r.d * 4 + 4) + r.d * 2 + 4)
+        res[name] = {
+            "shape": f"B={r.B} H={r.H} N={r.N} d={r.d} causal={r.causal}", "splits": S,
+            "fa_fwd_ms": round(ms_plain, 4), "fa_fwd_tflops": round(f / ms_plain / 1e9, 1),
+            "splitkv_ms": round(ms_split, 4), "splitkv_tflops": round(f / ms_split / 1e9, 1),
+            "merge_ms": round(ms_merge, 4),
+            "merge_roofline": {"bound": "hbm", "achieved": round(merge_bytes / ms_merge / 1e6, 1),
+                               "peak": 8000.0, "unit": "GB/s",
+                               "frac": round(merge_bytes / ms_merge / 1e6 / 8000.0, 4),
+                               "bytes_per_launch": merge_bytes},
+        }
+        del q, k, v, o, lse, op, lp
+    return res
 
 
 def traffic_for(fingerprint: str):
@@ -232,6 +281,7 @@ def main() -> int:
                 variants[f"{en}/{rn}"] = {"ms": round(kms, 4),
                                           "tflops": round(f / (kms * 1e-3) / 1e12, 1)}
         out["variants"] = variants
+        out["split_kv"] = split_kv_runs(torch, fa)
 
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")

@@ -30,6 +30,12 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb) {
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
+// The kernels address up to 64 rows of one tile with 32-bit byte offsets of
+// fp32 data: H * d * 4 * 64 must stay below 2^31.
+bool token_stride_ok(int H, int d) { return static_cast<long long>(H) * d <= (1LL << 22); }
+
+int key_tiles(int N) { return (N + kTileKeys - 1) / kTileKeys; }
+
 }  // namespace
 
 extern "C" {
@@ -45,6 +51,7 @@ const char *fa_strerror(int code) {
         case FA_ERR_VARIANT: return "exp_mode or rescale_mode out of range";
         case FA_ERR_ALIAS: return "an output overlaps an input or the other output";
         case FA_ERR_HIP: return "HIP kernel launch failed";
+        case FA_ERR_SPLIT: return "num_splits out of range (1 .. ceil(N / tile keys))";
         default: return "unknown fa status code";
     }
 }
@@ -69,7 +76,7 @@ int fa_fwd_variant(const void *q, const void *k, const void *v, void *o, float *
     const bool varlen = cu_seqlens != nullptr;
     const long long tokens = varlen ? static_cast<long long>(N) : static_cast<long long>(B) * N;
     const long long elems = tokens * H * d;
-    if (elems <= 0 || elems > (1LL << 46)) return FA_ERR_SHAPE;
+    if (elems <= 0 || elems > (1LL << 46) || !token_stride_ok(H, d)) return FA_ERR_SHAPE;
     const size_t tensor_bytes = static_cast<size_t>(elems) * 2;
     const size_t lse_bytes = static_cast<size_t>(tokens * H) * 4;
     if (overlap(o, tensor_bytes, q, tensor_bytes) || overlap(o, tensor_bytes, k, tensor_bytes) ||
@@ -78,7 +85,7 @@ int fa_fwd_variant(const void *q, const void *k, const void *v, void *o, float *
         overlap(lse, lse_bytes, o, tensor_bytes))
         return FA_ERR_ALIAS;
 
-    Params prm;
+    Params prm{};
     prm.q = static_cast<const uint16_t *>(q);
     prm.k = static_cast<const uint16_t *>(k);
     prm.v = static_cast<const uint16_t *>(v);
@@ -107,10 +114,146 @@ int fa_fwd_variant(const void *q, const void *k, const void *v, void *o, float *
     return FA_OK;
 }
 
+int fa_split_range(int N, int d, int causal, int num_splits, int s, int row, int *key_lo, int *key_hi) {
+    if (!key_lo || !key_hi) return FA_ERR_NULLPTR;
+    if (N < 1 || row < 0 || row >= N) return FA_ERR_SHAPE;
+    if (tile_rows_for(d) == 0) return FA_ERR_HEAD_DIM;
+    if (num_splits < 1 || num_splits > key_tiles(N) || s < 0 || s >= num_splits) return FA_ERR_SPLIT;
+    // keys the row's query tile sees: all, or up to the tile's last row
+    const long long rows = tile_rows_for(d);
+    const long long q_end = (row / rows + 1) * rows;
+    const long long seen = causal ? (q_end < N ? q_end : N) : N;
+    const long long t = (seen + kTileKeys - 1) / kTileKeys;
+    const long long lo = s * t / num_splits * kTileKeys, hi = (s + 1) * t / num_splits * kTileKeys;
+    *key_lo = static_cast<int>(lo);
+    *key_hi = static_cast<int>(hi < seen ? hi : seen);
+    return FA_OK;
+}
+
+int fa_num_splits(int B, int H, int N, int d, int causal, int num_cus) {
+    if (B < 1 || H < 1 || N < 1 || tile_rows_for(d) == 0) return 1;
+    const long long cus = num_cus > 0 ? num_cus : 256;
+    // workgroups resident per compute unit (LDS and registers): 3, 2, 1
+    const long long per_cu = d == 64 ? 3 : (d == 128 ? 2 : 1);
+    const long long slots = per_cu * cus;
+    const long long n_qt = (static_cast<long long>(N) + tile_rows_for(d) - 1) / tile_rows_for(d);
+    // causal: the average query tile sees half the keys
+    const long long wgs = static_cast<long long>(B) * H * n_qt / (causal ? 2 : 1);
+    if (wgs >= slots) return 1;
+    // with one workgroup per compute unit already, splitting pays only when
+    // each range stays long next to the partials it writes
+    if (wgs >= cus && N < 8192) return 1;
+    long long s = (slots + wgs - 1) / (wgs > 0 ? wgs : 1);
+    const long long cap = key_tiles(N) / 16 > 1 ? key_tiles(N) / 16 : 1;  // >= 1024 keys a range
+    if (s > cap) s = cap;
+    if (s > 32) s = 32;
+    return static_cast<int>(s < 1 ? 1 : s);
+}
+
+int fa_merge(const float *o_part, const float *lse_part, int num_splits, int B, int H, int N, int d,
+             void *o, float *lse, hipStream_t stream) {
+    if (!o_part || !lse_part || !o || !lse) return FA_ERR_NULLPTR;
+    if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128 && d != 256) return FA_ERR_HEAD_DIM;
+    if (num_splits < 1) return FA_ERR_SPLIT;
+    if (misaligned(o_part, 16) || misaligned(o, 16) || misaligned(lse_part, 4) || misaligned(lse, 4))
+        return FA_ERR_ALIGN;
+    const long long rows = static_cast<long long>(B) * N * H;
+    const long long elems = rows * d;
+    if (elems <= 0 || elems > (1LL << 46) || elems * num_splits > (1LL << 46)) return FA_ERR_SHAPE;
+    const size_t ob = static_cast<size_t>(elems) * 2, lb = static_cast<size_t>(rows) * 4;
+    const size_t opb = static_cast<size_t>(elems) * num_splits * 4, lpb = static_cast<size_t>(rows) * num_splits * 4;
+    if (overlap(o, ob, o_part, opb) || overlap(o, ob, lse_part, lpb) || overlap(lse, lb, o_part, opb) ||
+        overlap(lse, lb, lse_part, lpb) || overlap(o, ob, lse, lb))
+        return FA_ERR_ALIAS;
+    MergeParams mp;
+    mp.op = o_part;
+    mp.lp = lse_part;
+    mp.o = static_cast<uint16_t *>(o);
+    mp.lse = lse;
+    mp.rows = rows;
+    mp.ostride = elems;
+    mp.lstride = rows;
+    mp.H = H;
+    mp.N = N;
+    mp.nsplit = num_splits;
+    (void)hipGetLastError();
+    return launch_merge(mp, d, stream) == 0 ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                   int N, int d, float scale, int causal, int num_splits, float *o_part,
+                   float *lse_part, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !o_part || !lse_part) return FA_ERR_NULLPTR;
+    if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128 && d != 256) return FA_ERR_HEAD_DIM;
+    if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_SCALE;
+    if (num_splits < 1 || num_splits > key_tiles(N)) return FA_ERR_SPLIT;
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
+        misaligned(o_part, 16) || misaligned(lse, 4) || misaligned(lse_part, 4))
+        return FA_ERR_ALIGN;
+    const long long rows = static_cast<long long>(B) * N * H;
+    const long long elems = rows * d;
+    if (elems <= 0 || elems * num_splits > (1LL << 46) || !token_stride_ok(H, d)) return FA_ERR_SHAPE;
+    const size_t tb = static_cast<size_t>(elems) * 2, lb = static_cast<size_t>(rows) * 4;
+    const size_t opb = static_cast<size_t>(elems) * num_splits * 4, lpb = static_cast<size_t>(rows) * num_splits * 4;
+    const void *ins[3] = {q, k, v};
+    for (const void *in : ins)
+        if (overlap(o, tb, in, tb) || overlap(lse, lb, in, tb) || overlap(o_part, opb, in, tb) ||
+            overlap(lse_part, lpb, in, tb))
+            return FA_ERR_ALIAS;
+    if (overlap(o, tb, lse, lb) || overlap(o_part, opb, o, tb) || overlap(o_part, opb, lse, lb) ||
+        overlap(lse_part, lpb, o, tb) || overlap(lse_part, lpb, lse, lb) || overlap(o_part, opb, lse_part, lpb))
+        return FA_ERR_ALIAS;
+
+    Params prm{};
+    prm.q = static_cast<const uint16_t *>(q);
+    prm.k = static_cast<const uint16_t *>(k);
+    prm.v = static_cast<const uint16_t *>(v);
+    prm.o = static_cast<uint16_t *>(o);
+    prm.lse = lse;
+    prm.cu = nullptr;
+    prm.B = B;
+    prm.H = H;
+    prm.N = N;
+    prm.cs = scale * kLog2e;
+    const int rows_per_tile = tile_rows_for(d);
+    const long long n_qt = (static_cast<long long>(N) + rows_per_tile - 1) / rows_per_tile;
+    prm.n_qt = static_cast<int>(n_qt);
+    prm.op = o_part;
+    prm.lp = lse_part;
+    prm.nsplit = num_splits;
+    const long long grid = static_cast<long long>(B) * H * n_qt * num_splits;
+    if (grid <= 0 || grid > 0x7fffffffLL) return FA_ERR_SHAPE;
+
+    KernelFn fn;
+    switch (d) {
+        case 64: fn = select_split_d64(causal != 0); break;
+        case 128: fn = select_split_d128(causal != 0); break;
+        default: fn = select_split_d256(causal != 0); break;
+    }
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(grid)), dim3(kWorkgroupWaves * 64), 0, stream, prm);
+    if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+
+    MergeParams mp;
+    mp.op = o_part;
+    mp.lp = lse_part;
+    mp.o = static_cast<uint16_t *>(o);
+    mp.lse = lse;
+    mp.rows = rows;
+    mp.ostride = elems;
+    mp.lstride = rows;
+    mp.H = H;
+    mp.N = N;
+    mp.nsplit = num_splits;
+    return launch_merge(mp, d, stream) == 0 ? FA_OK : FA_ERR_HIP;
+}
+
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
            int d, float scale, int causal, const int32_t *cu_seqlens, hipStream_t stream) {
     return fa_fwd_variant(q, k, v, o, lse, B, H, N, d, scale, causal, cu_seqlens, stream,
-                          FA_EXP_HW, FA_RESCALE_STRICT);
+                          FA_EXP_HW, FA_RESCALE_THRESHOLD);
 }
 
 }  // extern "C"

@@ -15,6 +15,10 @@ struct Params {
     int B, H, N;        // N: sequence length (dense) or total tokens (packed)
     int n_qt;           // dense: query tiles per sequence
     float cs;           // scale * log2(e)
+    // split of the key sequence (split-KV instances only)
+    float *op;          // partial outputs, [nsplit][B*N][H][d] fp32
+    float *lp;          // partial LSEs, [nsplit][B][H][N] fp32
+    int nsplit;         // number of key ranges per query tile
 };
 
 using KernelFn = void (*)(Params);
@@ -42,5 +46,21 @@ inline int tile_rows_for(int d) {
 KernelFn select_d64(bool causal, bool varlen, int exp_mode, int rescale_mode);
 KernelFn select_d128(bool causal, bool varlen, int exp_mode, int rescale_mode);
 KernelFn select_d256(bool causal, bool varlen, int exp_mode, int rescale_mode);
+// Split-KV instance (dense layout, partial results into Params::op / lp).
+KernelFn select_split_d64(bool causal);
+KernelFn select_split_d128(bool causal);
+KernelFn select_split_d256(bool causal);
+
+// Merge of split-KV partials (fa_merge.hip).
+struct MergeParams {
+    const float *op, *lp;  // partials, layouts as in Params
+    uint16_t *o;           // bf16 [B*N][H][d]
+    float *lse;            // [B][H][N]
+    long long rows;        // B*N*H
+    long long ostride;     // elements between splits of op
+    long long lstride;     // elements between splits of lp
+    int H, N, nsplit;
+};
+int launch_merge(const MergeParams &mp, int d, void *stream);
 
 }  // namespace fa_detail

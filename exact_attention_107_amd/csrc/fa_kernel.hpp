@@ -58,6 +58,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -192,12 +193,45 @@ __device__ __forceinline__ void static_for(F &&f) {
 struct Work {
     int b, h, qt, n;  // n: length of sequence b
     long long t0;     // first token of sequence b
+    int split;        // key range (split-KV instances)
 };
 
-template <bool CAUSAL, bool VARLEN, int BR>
+template <bool CAUSAL, bool VARLEN, int BR, bool SPLIT>
 __device__ __forceinline__ bool decode_work(const Params &p, Work &w) {
     const int wg = blockIdx.x;
-    if constexpr (!VARLEN) {
+    w.split = 0;
+    if constexpr (SPLIT) {
+        // Items are (b, h, key range, query tile); the ranges of one query
+        // tile hold equal work.  Causal: highest query tile first (it sees the
+        // most keys).  Non-causal: each XCD
+        // gets a contiguous run of items, i.e. the query tiles of one
+        // (b, h, range) and so one K/V range in its L2.
+        const int BH = p.B * p.H, S = p.nsplit;
+        int bh, qt, s;
+        if constexpr (CAUSAL) {
+            const int level = BH * S;
+            qt = p.n_qt - 1 - wg / level;
+            const int r = wg - (wg / level) * level;
+            s = r / BH;
+            bh = r - s * BH;
+        } else {
+            const int G = gridDim.x, x = wg & 7, sx = wg >> 3;
+            const int per = G >> 3, rem = G & 7;
+            const int item = x * per + (x < rem ? x : rem) + sx;
+            const int per_bh = S * p.n_qt;
+            bh = item / per_bh;
+            const int r = item - bh * per_bh;
+            s = r / p.n_qt;
+            qt = r - s * p.n_qt;
+        }
+        w.b = bh / p.H;
+        w.h = bh - w.b * p.H;
+        w.qt = qt;
+        w.split = s;
+        w.n = p.N;
+        w.t0 = static_cast<long long>(w.b) * p.N;
+        return true;
+    } else if constexpr (!VARLEN) {
         const int BH = p.B * p.H;
         int bh, qt;
         if constexpr (CAUSAL) {
@@ -290,7 +324,7 @@ __device__ __forceinline__ bool decode_work(const Params &p, Work &w) {
 // consumed before the previous barrier); the barrier that ends the iteration
 // makes them visible.
 
-template <int D, int BC, int NW, int QB, bool CAUSAL, bool VARLEN, int EXPM, int RSM>
+template <int D, int BC, int NW, int QB, bool CAUSAL, bool VARLEN, int EXPM, int RSM, bool SPLIT = false>
 __global__ void __launch_bounds__(NW * 64)
 fa_fwd_kernel(Params p) {
     using SW = Swz<D>;
@@ -314,7 +348,7 @@ fa_fwd_kernel(Params p) {
     __shared__ __attribute__((aligned(1024))) char k_lds0[TB], k_lds1[TB], v_lds0[TB], v_lds1[TB];
 
     Work w;
-    if (!decode_work<CAUSAL, VARLEN, BR>(p, w)) return;
+    if (!decode_work<CAUSAL, VARLEN, BR, SPLIT>(p, w)) return;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -345,9 +379,17 @@ fa_fwd_kernel(Params p) {
     }
 
     const int kv_end = CAUSAL ? min(n, q0 + BR) : n;
-    const int nkv = (kv_end + BC - 1) / BC;
+    // Tiles are numbered from kt0, the first tile of this workgroup's key
+    // range (0 unless the key sequence is split); tile j covers keys
+    // (kt0 + j) * BC ...
+    // The split divides the tiles this query tile sees (all of the sequence,
+    // or up to the diagonal when causal) into nsplit near-equal ranges.
+    const int tiles_seen = (kv_end + BC - 1) / BC;
+    const int kt0 = SPLIT ? w.split * tiles_seen / p.nsplit : 0;
+    const int kt_end = SPLIT ? (w.split + 1) * tiles_seen / p.nsplit : tiles_seen;
+    const int nkv = max(kt_end - kt0, 0);
     // tiles this wave computes: the causal diagonal ends its work earlier
-    const int nkv_w = CAUSAL ? min(nkv, (wrow0 + RW - 1) / BC + 1) : nkv;
+    const int nkv_w = CAUSAL ? max(min(kt_end, (wrow0 + RW - 1) / BC + 1) - kt0, 0) : nkv;
 
     // ---- direct global -> LDS loads ---------------------------------------------
     // K: the tile is 8*D/64 loads of 1 KB (8 rows of one 128-byte plane each);
@@ -375,7 +417,7 @@ fa_fwd_kernel(Params p) {
         voff = r * rs_bytes + ((pc ^ Swz<D>::fv(r)) << 4);
     }
     auto dma_k = [&](char *tile, int j) {
-        const int kv0 = j * BC;
+        const int kv0 = (kt0 + j) * BC;
         const auto rsrc = make_rsrc(kg + kv0 * rs, (long long)(n - kv0) * rs_bytes);
 #pragma unroll
         for (int i = 0; i < KPW; ++i) {
@@ -387,7 +429,7 @@ fa_fwd_kernel(Params p) {
     };
     constexpr int VROWS = 1024 / RB;     // V rows per 1 KB block
     auto dma_v = [&](char *tile, int j) {
-        const int kv0 = j * BC;
+        const int kv0 = (kt0 + j) * BC;
         const auto rsrc = make_rsrc(vg + kv0 * rs, (long long)(n - kv0) * rs_bytes);
 #pragma unroll
         for (int i = 0; i < BPW; ++i)
@@ -446,11 +488,11 @@ fa_fwd_kernel(Params p) {
 
     // -inf for tail keys (>= n) and, when causal, keys after the query.
     auto need_mask = [&](int j) {
-        const int kv0 = j * BC;
+        const int kv0 = (kt0 + j) * BC;
         return (CAUSAL && kv0 + BC - 1 > wrow0) || kv0 + BC > n;
     };
     auto s_mask = [&](f32x16 (&s)[QB][NKB], int j) {
-        const int kv0 = j * BC;
+        const int kv0 = (kt0 + j) * BC;
 #pragma unroll
         for (int b = 0; b < QB; ++b) {
             const int qrow = wrow0 + 32 * b + c;
@@ -670,6 +712,9 @@ fa_fwd_kernel(Params p) {
 
     // ---- prologue: K_0, V_0, K_1 into LDS; S_0 and its row max ------------------
     f32x16 sa[QB][NKB], sb[QB][NKB];
+    // (a key range with no visible key for the workgroup skips straight to the
+    // epilogue and stores the empty result)
+    if (nkv > 0) {
     dma_k(k_lds0, 0);
     dma_v(v_lds0, 0);
     if (nkv > 1) dma_k(k_lds1, 1);
@@ -727,7 +772,7 @@ fa_fwd_kernel(Params p) {
     using Mask = std::integral_constant<bool, true>;
 
     // first tile that needs a mask (tail: n / BC; causal: (wrow0 + 1) / BC)
-    const int jm = CAUSAL ? min(n / BC, (wrow0 + 1) / BC) : n / BC;
+    const int jm = (CAUSAL ? min(n / BC, (wrow0 + 1) / BC) : n / BC) - kt0;
     const int lim = min(nkv_w, jm);
     int j = 0;
     // hot loop: pairs of full steps whose next tiles need no mask
@@ -755,6 +800,7 @@ fa_fwd_kernel(Params p) {
         issue_loads(j, ((j & 1) ? k_lds1 : k_lds0), ((j & 1) ? v_lds0 : v_lds1));
         end_iteration();
     }
+    }  // nkv > 0
 
     // ---- epilogue: O / l, LSE = (m + log2 l) ln 2 ----------------------------
 #pragma unroll
@@ -763,6 +809,30 @@ fa_fwd_kernel(Params p) {
         const float l = xhalf_sum(l_run[b]);
         // rows >= n fall outside the buffer and are dropped
         const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+        if constexpr (SPLIT) {
+            // normalised fp32 partial O of this key range, and its LSE
+            const long long sbase = static_cast<long long>(w.split) * p.B * p.N * p.H * D + base;
+            const auto prs = make_rsrc(p.op + sbase + rowb * rs, (long long)(n - rowb) * rs * 4);
+            const int voff_p = c * static_cast<int>(rs) * 4;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int col = db * 32 + g4 * 8 + hh * 4;
+                    const f32x4 v4 = {oacc[b][db][g4 * 4 + 0] * inv, oacc[b][db][g4 * 4 + 1] * inv,
+                                      oacc[b][db][g4 * 4 + 2] * inv, oacc[b][db][g4 * 4 + 3] * inv};
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v4), prs,
+                                                           voff_p + col * 4, 0, 0);
+                }
+            }
+            const int qrow = rowb + c;
+            if (qrow < n && hh == 0) {
+                const float lse = l > 0.0f ? (m_run[b] + log2f(l)) * kLn2 : -INFINITY;
+                p.lp[(static_cast<long long>(w.split) * p.B * p.H + static_cast<long long>(w.b) * p.H + w.h) *
+                         p.N + qrow] = lse;
+            }
+            continue;
+        }
         const auto ors = make_rsrc(p.o + base + rowb * rs, (long long)(n - rowb) * rs * 2);
         const int voff_o = c * static_cast<int>(rs) * 2;
 #pragma unroll
@@ -806,6 +876,13 @@ KernelFn select_exp(int expm, int rsm) {
         case FA_EXP_POLY: return select_rsm<D, CAUSAL, VARLEN, FA_EXP_POLY>(rsm);
         default: return select_rsm<D, CAUSAL, VARLEN, FA_EXP_MIXED>(rsm);
     }
+}
+
+template <int D>
+KernelFn select_split(bool causal) {
+    constexpr int BC = kTileKeys, NW = kWorkgroupWaves, QB = Geometry<D>::kBlocks;
+    if (causal) return fa_fwd_kernel<D, BC, NW, QB, true, false, FA_EXP_HW, FA_RESCALE_THRESHOLD, true>;
+    return fa_fwd_kernel<D, BC, NW, QB, false, false, FA_EXP_HW, FA_RESCALE_THRESHOLD, true>;
 }
 
 template <int D>

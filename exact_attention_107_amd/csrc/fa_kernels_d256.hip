@@ -7,4 +7,6 @@ KernelFn select_d256(bool causal, bool varlen, int exp_mode, int rescale_mode) {
     return select_kernel<256>(causal, varlen, exp_mode, rescale_mode);
 }
 
+KernelFn select_split_d256(bool causal) { return select_split<256>(causal); }
+
 }  // namespace fa_detail

@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 # enum fa_exp_mode / fa_rescale_mode of include/fa.h
 EXP_HW, EXP_POLY, EXP_MIXED = 0, 1, 2
 RESCALE_ALWAYS, RESCALE_STRICT, RESCALE_THRESHOLD = 0, 1, 2
-EXPORTS = ("fa_fwd", "fa_fwd_variant", "fa_strerror", "fa_tile_rows", "fa_tile_keys")
+EXPORTS = ("fa_fwd", "fa_fwd_variant", "fa_strerror", "fa_tile_rows", "fa_tile_keys",
+           "fa_fwd_splitkv", "fa_merge", "fa_split_range", "fa_num_splits")
 
 _lib = None
 
@@ -51,6 +52,15 @@ def load(path: str | None = None):
     lib.fa_tile_rows.restype = i32
     lib.fa_tile_keys.argtypes = [i32]
     lib.fa_tile_keys.restype = i32
+    lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_float, i32,
+                                   i32, vp, vp, vp]
+    lib.fa_fwd_splitkv.restype = i32
+    lib.fa_merge.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
+    lib.fa_merge.restype = i32
+    lib.fa_split_range.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.fa_split_range.restype = i32
+    lib.fa_num_splits.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.fa_num_splits.restype = i32
     if path is None:
         _lib = lib
     return lib
@@ -133,7 +143,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
             rc = lib.fa_fwd(*args)
         else:
             rc = lib.fa_fwd_variant(*args, int(EXP_HW if exp_mode is None else exp_mode),
-                                    int(RESCALE_STRICT if rescale_mode is None else rescale_mode))
+                                    int(RESCALE_THRESHOLD if rescale_mode is None else rescale_mode))
     if rc != 0:
         raise FaError(rc, strerror(rc))
     return out, lse
@@ -145,3 +155,99 @@ def tile_rows(d: int) -> int:
 
 def tile_keys(d: int) -> int:
     return int(load().fa_tile_keys(int(d)))
+
+
+def split_range(N: int, d: int, causal: bool, num_splits: int, s: int, row: int) -> tuple[int, int]:
+    """Keys ``[lo, hi)`` of range ``s`` of :func:`fwd_splitkv` for query ``row``."""
+    lo, hi = ctypes.c_int(), ctypes.c_int()
+    rc = load().fa_split_range(int(N), int(d), int(bool(causal)), int(num_splits), int(s), int(row),
+                               ctypes.byref(lo), ctypes.byref(hi))
+    if rc != 0:
+        raise FaError(rc, strerror(rc))
+    return lo.value, hi.value
+
+
+def num_splits(B: int, H: int, N: int, d: int, causal: bool = False, num_cus: int = 0) -> int:
+    """The library's suggested split count for :func:`fwd_splitkv`."""
+    return int(load().fa_num_splits(int(B), int(H), int(N), int(d), int(bool(causal)), int(num_cus)))
+
+
+def _dense_shape(q):
+    if q.dim() != 4:
+        raise ValueError("split-KV tensors are dense [B, N, H, d]")
+    return tuple(int(x) for x in q.shape)
+
+
+def fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+                scale: float | None = None, splits: int | None = None,
+                out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                o_part: torch.Tensor | None = None, lse_part: torch.Tensor | None = None,
+                stream: torch.cuda.Stream | None = None):
+    """Split-KV forward (``fa_fwd_splitkv``), dense ``[B, N, H, d]`` only.
+
+    ``splits`` defaults to the library's suggestion for this device.  The fp32
+    workspaces ``o_part [S, B, N, H, d]`` and ``lse_part [S, B, H, N]`` are
+    allocated with torch unless given.  Returns ``(o, lse)``.
+    """
+    lib = load()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a GPU tensor")
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, name, torch.bfloat16, dev)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must have the same shape")
+    B, N, H, d = _dense_shape(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if splits is None:
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        splits = num_splits(B, H, N, d, causal, cus)
+    S = int(splits)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if lse is None else lse
+    o_part = torch.empty((S, B, N, H, d), dtype=torch.float32, device=dev) if o_part is None else o_part
+    lse_part = torch.empty((S, B, H, N), dtype=torch.float32, device=dev) if lse_part is None else lse_part
+    for t, name, dt, shape in ((out, "out", torch.bfloat16, (B, N, H, d)),
+                               (lse, "lse", torch.float32, (B, H, N)),
+                               (o_part, "o_part", torch.float32, (S, B, N, H, d)),
+                               (lse_part, "lse_part", torch.float32, (S, B, H, N))):
+        _check(t, name, dt, dev)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be {shape}")
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                B, H, N, d, ctypes.c_float(scale), int(bool(causal)), S,
+                                o_part.data_ptr(), lse_part.data_ptr(), ctypes.c_void_p(s.cuda_stream))
+    if rc != 0:
+        raise FaError(rc, strerror(rc))
+    return out, lse
+
+
+def merge(o_part: torch.Tensor, lse_part: torch.Tensor, *, out: torch.Tensor | None = None,
+          lse: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None):
+    """``fa_merge``: combine fp32 partials ``o_part [S, B, N, H, d]`` and
+    ``lse_part [S, B, H, N]`` into bf16 ``o`` and fp32 ``lse``."""
+    lib = load()
+    dev = o_part.device
+    _check(o_part, "o_part", torch.float32, dev)
+    _check(lse_part, "lse_part", torch.float32, dev)
+    if o_part.dim() != 5:
+        raise ValueError("o_part must be [S, B, N, H, d]")
+    S, B, N, H, d = (int(x) for x in o_part.shape)
+    if tuple(lse_part.shape) != (S, B, H, N):
+        raise ValueError("lse_part must be [S, B, H, N]")
+    out = torch.empty((B, N, H, d), dtype=torch.bfloat16, device=dev) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if lse is None else lse
+    _check(out, "out", torch.bfloat16, dev)
+    _check(lse, "lse", torch.float32, dev)
+    if tuple(out.shape) != (B, N, H, d) or tuple(lse.shape) != (B, H, N):
+        raise ValueError("out must be [B, N, H, d] and lse [B, H, N]")
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = lib.fa_merge(o_part.data_ptr(), lse_part.data_ptr(), S, B, H, N, d, out.data_ptr(),
+                          lse.data_ptr(), ctypes.c_void_p(s.cuda_stream))
+    if rc != 0:
+        raise FaError(rc, strerror(rc))
+    return out, lse

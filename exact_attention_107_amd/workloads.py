@@ -6,7 +6,8 @@ can take their inputs from it.
 
 The pages give no workload shapes; the runs below are the library's own test
 and benchmark set (dense, causal, long causal, packed variable-length causal,
-and a wide-logit stress input).  Every draw is numpy ``Generator(PCG64(seed))``
+a wide-logit stress input, and few-head long sequences for the split of the
+key sequence).  Every draw is numpy ``Generator(PCG64(seed))``
 fp32 ``standard_normal`` (times sigma where stated), then rounded once to
 bf16 round-to-nearest-even.  Tensor order is Q, K, V.
 """
@@ -64,6 +65,10 @@ RUNS = {
     "wide": Run("wide", 2, 16, 8192, 128, False, 1005, sigma_qk=3.0, boost_frac=0.01),
     "wide_d64": Run("wide_d64", 2, 16, 4096, 64, False, 1005, sigma_qk=3.0, boost_frac=0.01),
     "wide_d256": Run("wide_d256", 2, 16, 4096, 256, False, 1005, sigma_qk=3.0, boost_frac=0.01),
+    # few (batch, head) pairs over long sequences: too few query tiles to fill
+    # the GPU, the shape the split of the key sequence is for
+    "few_heads": Run("few_heads", 1, 4, 8192, 128, False, 1006),
+    "few_heads_causal": Run("few_heads_causal", 1, 4, 16384, 128, True, 1007),
 }
 
 

@@ -68,7 +68,8 @@ enum fa_status {
                             not 4-byte aligned                                  */
     FA_ERR_VARIANT = 6,  /* exp_mode or rescale_mode out of range               */
     FA_ERR_ALIAS = 7,    /* o or lse overlaps an input or each other            */
-    FA_ERR_HIP = 8       /* the HIP launch itself failed                        */
+    FA_ERR_HIP = 8,      /* the HIP launch itself failed                        */
+    FA_ERR_SPLIT = 9     /* num_splits outside 1 .. ceil(N / fa_tile_keys(d))   */
 };
 
 /* How P~ = exp(s - m) is evaluated (section 3.2 of the FlashAttention V4
@@ -97,7 +98,7 @@ enum fa_rescale_mode {
  *   o         device bf16 output, same shape as q.
  *   lse       device fp32 output, [B, H, N] (dense) or [H, T] (packed).
  *   B         batch size (dense) or number of packed sequences, >= 1.
- *   H         heads, >= 1.
+ *   H         heads, >= 1, with H * d <= 4194304.
  *   N         sequence length (dense) or total tokens T (packed), >= 1.
  *   d         head dimension: 64, 128 or 256.
  *   scale     softmax scale applied to Q K^T in fp32 (usually 1/sqrt(d)),
@@ -107,7 +108,9 @@ enum fa_rescale_mode {
  *             offsets with cu_seqlens[0] = 0 and cu_seqlens[B] = N.
  *   stream    HIP stream the kernel is queued on (NULL: default stream).
  * Returns FA_OK or an fa_status code.  Uses the library's default variant
- * (hardware exp, strict conditional rescale).
+ * (hardware exp, threshold conditional rescale: the fastest variant measured
+ * on every shape tried; strict and threshold give the same O and LSE up to
+ * rounding).
  */
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
            int B, int H, int N, int d, float scale, int causal,
@@ -122,6 +125,72 @@ int fa_fwd_variant(const void *q, const void *k, const void *v, void *o,
                    float *lse, int B, int H, int N, int d, float scale,
                    int causal, const int32_t *cu_seqlens, hipStream_t stream,
                    int exp_mode, int rescale_mode);
+
+/*
+ * Split-KV forward (dense layout only).  For every (b, h) and query tile of
+ * fa_tile_rows(d) rows, the keys that tile sees (all N, or when causal those
+ * up to its last row) are cut into num_splits consecutive ranges of whole
+ * K/V tiles of near-equal length: with T such tiles, range s holds tiles
+ * [floor(s T / num_splits), floor((s + 1) T / num_splits)) (fa_split_range
+ * gives the keys; a range is empty when T < num_splits).  Each (query tile,
+ * key range) pair is a
+ * workgroup of its own, so the launch has num_splits times more parallel
+ * work than fa_fwd: the parallelisation along the key sequence that the
+ * FlashAttention-2 section of "FlashAttention 1-4 explained" describes, for
+ * shapes whose B * H * ceil(N / fa_tile_rows(d)) workgroups cannot fill the
+ * GPU.  A first kernel writes, per key range, the attention of every query
+ * row over that range alone; a second (fa_merge) combines them.
+ *
+ *   q, k, v, o, lse, B, H, N, d, scale, causal   as fa_fwd (dense layout).
+ *   num_splits  1 .. ceil(N / fa_tile_keys(d)); fa_num_splits suggests one.
+ *   o_part      device fp32 workspace, [num_splits, B, N, H, d]
+ *               (num_splits * B * N * H * d floats, 16-byte aligned).
+ *               On return (after the stream work) it holds each range's
+ *               normalised partial output; 0 for rows that see no key of
+ *               the range (causal).
+ *   lse_part    device fp32 workspace, [num_splits, B, H, N]; each range's
+ *               partial LSE, -inf for rows that see no key of the range.
+ * The workspaces belong to the caller, like every other buffer, and must
+ * not overlap any input, output or each other.  O and LSE equal fa_fwd's up
+ * to rounding (the fp32 partials are rounded to bf16 only after the merge).
+ * Uses hardware exp and the threshold rescale.
+ */
+int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o,
+                   float *lse, int B, int H, int N, int d, float scale,
+                   int causal, int num_splits, float *o_part, float *lse_part,
+                   hipStream_t stream);
+
+/*
+ * fa_merge: the combination step of fa_fwd_splitkv, usable on its own (for
+ * example on partials computed over key shards held elsewhere).  For each
+ * row, with LSE_s and O_s the partials of range s,
+ *     LSE = ln sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s,
+ * which is exact because each O_s is a softmax-weighted mean over its own
+ * keys.  A row whose partials are all empty (LSE_s = -inf) gets O = 0 and
+ * LSE = -inf.
+ *   o_part, lse_part  device fp32 partials, layouts as in fa_fwd_splitkv.
+ *   o, lse            device outputs: bf16 [B, N, H, d], fp32 [B, H, N].
+ * Errors as fa_fwd (FA_ERR_SPLIT for num_splits < 1).
+ */
+int fa_merge(const float *o_part, const float *lse_part, int num_splits,
+             int B, int H, int N, int d, void *o, float *lse,
+             hipStream_t stream);
+
+/* Keys [*key_lo, *key_hi) of range s of fa_fwd_splitkv for query row `row`
+ * (the range of its query tile; the row itself, when causal, sees only the
+ * keys <= row of it).  Returns FA_OK, FA_ERR_NULLPTR, FA_ERR_SHAPE (N < 1 or
+ * row outside [0, N)), FA_ERR_HEAD_DIM or FA_ERR_SPLIT (num_splits or s out
+ * of range). */
+int fa_split_range(int N, int d, int causal, int num_splits, int s, int row,
+                   int *key_lo, int *key_hi);
+
+/* A split count for fa_fwd_splitkv on a GPU with num_cus compute units
+ * (<= 0: 256).  Returns 1 (use fa_fwd) when fa_fwd's workgroups (counted
+ * half when causal) already fill every resident slot (3, 2 or 1 workgroups
+ * per compute unit at d = 64, 128, 256), or fill one per compute unit and
+ * N < 8192; otherwise enough ranges to fill the slots, each at least 1024
+ * keys long, at most 32. */
+int fa_num_splits(int B, int H, int N, int d, int causal, int num_cus);
 
 /* Static, NUL-terminated description of an fa_status code. */
 const char *fa_strerror(int code);

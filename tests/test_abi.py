@@ -13,7 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
 
 # fa_status codes of include/fa.h
-OK, NULLPTR, SHAPE, HEAD_DIM, SCALE, ALIGN, VARIANT, ALIAS, HIP = range(9)
+OK, NULLPTR, SHAPE, HEAD_DIM, SCALE, ALIGN, VARIANT, ALIAS, HIP, SPLIT = range(10)
 
 
 def header_functions():
@@ -46,6 +46,7 @@ def test_exports_every_header_function(lib):
 def test_enum_values_match_binding():
     st = header_enum("fa_status")
     assert st["FA_OK"] == OK and st["FA_ERR_HIP"] == HIP and st["FA_ERR_ALIAS"] == ALIAS
+    assert st["FA_ERR_SPLIT"] == SPLIT and len(st) == 10
     ex = header_enum("fa_exp_mode")
     assert (ex["FA_EXP_HW"], ex["FA_EXP_POLY"], ex["FA_EXP_MIXED"]) == (fa.EXP_HW, fa.EXP_POLY, fa.EXP_MIXED)
     rs = header_enum("fa_rescale_mode")
@@ -54,7 +55,7 @@ def test_enum_values_match_binding():
 
 
 def test_strerror(lib):
-    for code in range(9):
+    for code in range(10):
         s = fa.strerror(code)
         assert isinstance(s, str) and s
     assert "unknown" in fa.strerror(1234)
@@ -85,7 +86,7 @@ def call(lib, q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, N=64, d=128, scale=0.125, cau
     (dict(q=0), NULLPTR), (dict(k=0), NULLPTR), (dict(v=0), NULLPTR), (dict(o=0), NULLPTR),
     (dict(lse=0), NULLPTR),
     (dict(B=0), SHAPE), (dict(H=0), SHAPE), (dict(N=0), SHAPE), (dict(N=-5), SHAPE),
-    (dict(B=1 << 20, H=1 << 10, N=1 << 20), SHAPE),
+    (dict(B=1 << 20, H=1 << 10, N=1 << 20), SHAPE), (dict(H=(1 << 22) // 128 + 1), SHAPE),
     (dict(d=96), HEAD_DIM), (dict(d=0), HEAD_DIM), (dict(d=512), HEAD_DIM),
     (dict(scale=0.0), SCALE), (dict(scale=-0.1), SCALE), (dict(scale=float("inf")), SCALE),
     (dict(scale=float("nan")), SCALE),
@@ -102,3 +103,95 @@ def test_python_binding_checks():
     x = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.fwd(x, x, x)  # not a GPU tensor
+
+
+# workspaces for the split-KV calls (fake addresses, far from the others)
+OP, LP = 0x10000000, 0x20000000
+
+
+def call_split(lib, q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, N=1000, d=128, scale=0.125, causal=0,
+               splits=4, op=OP, lp=LP):
+    return lib.fa_fwd_splitkv(ctypes.c_void_p(q), ctypes.c_void_p(k), ctypes.c_void_p(v),
+                              ctypes.c_void_p(o), ctypes.c_void_p(lse), B, H, N, d,
+                              ctypes.c_float(scale), causal, splits, ctypes.c_void_p(op),
+                              ctypes.c_void_p(lp), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), NULLPTR), (dict(op=0), NULLPTR), (dict(lp=0), NULLPTR),
+    (dict(B=0), SHAPE), (dict(d=32), HEAD_DIM), (dict(scale=float("nan")), SCALE),
+    (dict(splits=0), SPLIT), (dict(splits=-1), SPLIT), (dict(splits=17), SPLIT),  # 1000 keys = 16 tiles
+    (dict(op=OP + 8), ALIGN), (dict(lp=LP + 1), ALIGN),
+    (dict(op=Q), ALIAS), (dict(lp=K), ALIAS), (dict(op=O - 64), ALIAS), (dict(lp=L), ALIAS),
+    (dict(lp=OP + 4 * 1000 * 2 * 128), ALIAS),  # inside split 0 of o_part
+])
+def test_splitkv_invalid_arguments_are_rejected(lib, kw, code):
+    assert call_split(lib, **kw) == code
+
+
+def call_merge(lib, op=OP, lp=LP, splits=3, B=1, H=2, N=100, d=64, o=O, lse=L):
+    return lib.fa_merge(ctypes.c_void_p(op), ctypes.c_void_p(lp), splits, B, H, N, d,
+                        ctypes.c_void_p(o), ctypes.c_void_p(lse), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(op=0), NULLPTR), (dict(o=0), NULLPTR), (dict(splits=0), SPLIT), (dict(N=0), SHAPE),
+    (dict(d=100), HEAD_DIM), (dict(op=OP + 4), ALIGN), (dict(o=O + 2), ALIGN),
+    (dict(o=OP + 1024), ALIAS), (dict(lse=LP), ALIAS),
+])
+def test_merge_invalid_arguments_are_rejected(lib, kw, code):
+    assert call_merge(lib, **kw) == code
+
+
+def test_split_range(lib):
+    # non-causal: every query tile splits all T = ceil(N / 64) tiles,
+    # range s = tiles [floor(s T / S), floor((s + 1) T / S)), cut at N
+    assert fa.split_range(1000, 128, False, 4, 0, 5) == (0, 256)
+    assert fa.split_range(1000, 128, False, 4, 3, 999) == (768, 1000)
+    assert fa.split_range(1000, 128, False, 3, 1, 0) == (320, 640)
+    # causal: the tile of rows 128..255 sees keys < 256 (4 tiles)
+    assert fa.split_range(1000, 128, True, 2, 0, 130) == (0, 128)
+    assert fa.split_range(1000, 128, True, 2, 1, 255) == (128, 256)
+    # the last tile sees up to N
+    assert fa.split_range(1000, 128, True, 2, 1, 999) == (512, 1000)
+    for N in (1, 63, 64, 65, 1000, 8191):
+        tiles = -(-N // 64)
+        for causal in (False, True):
+            for S in range(1, min(tiles, 20) + 1):
+                for row in sorted({0, N // 3, N - 1}):
+                    seen = min(N, (row // 128 + 1) * 128) if causal else N
+                    ranges = [fa.split_range(N, 128, causal, S, s, row) for s in range(S)]
+                    # consecutive, tile-aligned, covering [0, seen), near-equal
+                    assert ranges[0][0] == 0 and ranges[-1][1] == seen, (N, S, row, ranges)
+                    for (a, b), (c, _) in zip(ranges, ranges[1:]):
+                        assert b == c and a % 64 == 0 and b >= a
+                    full = [b - a for a, b in ranges[:-1]]
+                    assert not full or max(full) - min(full) <= 64
+    for bad in ((1000, 128, False, 17, 0, 0), (1000, 128, False, 0, 0, 0), (1000, 128, False, 4, 4, 0),
+                (1000, 128, False, 4, -1, 0), (0, 128, False, 1, 0, 0), (1000, 128, False, 1, 0, 1000),
+                (1000, 96, False, 1, 0, 0)):
+        with pytest.raises(fa.FaError):
+            fa.split_range(*bad)
+
+
+def test_num_splits_heuristic(lib):
+    # fa_fwd already fills every resident slot: no split
+    assert fa.num_splits(2, 16, 8192, 128, False, 256) == 1
+    # one head of 8192 keys: 64 query tiles for 512 slots -> 8 ranges of 1024 keys
+    assert fa.num_splits(1, 1, 8192, 128, False, 256) == 8
+    # one workgroup per CU already: split only long sequences
+    assert fa.num_splits(1, 4, 8192, 128, False, 256) == 2
+    assert fa.num_splits(1, 8, 4096, 128, False, 256) == 1
+    # ranges of at least 1024 keys
+    assert fa.num_splits(1, 1, 512, 128, False, 256) == 1
+    assert fa.num_splits(1, 1, 2048, 128, False, 256) == 2
+    # d = 64 keeps 3 workgroups per CU resident, d = 256 one
+    assert fa.num_splits(1, 1, 1 << 16, 64, False, 256) == 2
+    assert fa.num_splits(1, 4, 8192, 256, False, 256) == 1
+    # never more than 32, never < 1
+    assert fa.num_splits(1, 1, 1 << 16, 128, False, 8192) == 32
+    assert fa.num_splits(1, 1, 1, 128, False, 256) == 1
+    assert fa.num_splits(0, 1, 100, 128, False, 256) == 1
+    # causal counts half the workgroups
+    assert fa.num_splits(1, 4, 16384, 128, True, 256) == 2
+    assert fa.num_splits(1, 8, 16384, 128, True, 256) == 1
