@@ -5,7 +5,7 @@ against.  Only the tests, the smoke check and the CPU-baseline leg of the
 benchmark may import it; the product path never does, and nothing here is
 shared with the HIP path.
 
-Two functions, both written from the FlashAttention explainer pages:
+The forward, written from the FlashAttention explainer pages:
 
 * :func:`attention` -- the plain definition (compute chain of section 1.1;
   the "standard attention" equations of the FlashAttention 1-4 post): each
@@ -14,6 +14,9 @@ Two functions, both written from the FlashAttention explainer pages:
 * :func:`oracle.online.online_attention` -- the tiled online-softmax
   recurrence of the FlashAttention-1 derivation, used only to cross-check the
   definition (the two agree to rounding in exact arithmetic).
+
+and :func:`oracle.backward.attention_backward`, the exact gradients of the
+same definition (numpy, fp64), for the backward pass.
 
 Layouts: dense tensors are ``[B, N, H, d]`` uint16 (bf16 bit patterns);
 packed variable-length tensors are ``[T, H, d]`` with ``cu_seqlens`` (int32,
@@ -84,6 +87,14 @@ def default_threads() -> int:
 
 def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
+
+
+def _widen(x) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64, exactly; float arrays -> float64."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
 
 
 def all_rows(B: int, H: int, lengths) -> np.ndarray:
