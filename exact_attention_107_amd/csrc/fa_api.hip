@@ -250,6 +250,70 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
     return launch_merge(mp, d, stream) == 0 ? FA_OK : FA_ERR_HIP;
 }
 
+long long fa_bwd_workspace_floats(int B, int H, int N) {
+    if (B < 1 || H < 1 || N < 1) return 0;
+    return static_cast<long long>(B) * H * ((N + 31) / 32) * 64;
+}
+
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
+           void *dq, void *dk, void *dv, int B, int H, int N, int d, float scale, int causal,
+           float *workspace, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return FA_ERR_NULLPTR;
+    if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+    if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_SCALE;
+    const void *t16[] = {q, k, v, o, dout, dq, dk, dv, workspace};
+    for (const void *t : t16)
+        if (misaligned(t, 16)) return FA_ERR_ALIGN;
+    if (misaligned(lse, 4)) return FA_ERR_ALIGN;
+    const long long rows = static_cast<long long>(B) * N * H;
+    const long long elems = rows * d;
+    if (elems <= 0 || elems > (1LL << 46) || !token_stride_ok(H, d)) return FA_ERR_SHAPE;
+    const size_t tb = static_cast<size_t>(elems) * 2, lb = static_cast<size_t>(rows) * 4;
+    const size_t wb = static_cast<size_t>(fa_bwd_workspace_floats(B, H, N)) * 4;
+    const void *outs[] = {dq, dk, dv, workspace};
+    const size_t out_bytes[] = {tb, tb, tb, wb};
+    const void *ins[] = {q, k, v, o, dout, lse};
+    const size_t in_bytes[] = {tb, tb, tb, tb, tb, lb};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlap(outs[i], out_bytes[i], ins[j], in_bytes[j])) return FA_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], out_bytes[i], outs[j], out_bytes[j])) return FA_ERR_ALIAS;
+    }
+
+    BwdParams bp{};
+    bp.q = static_cast<const uint16_t *>(q);
+    bp.k = static_cast<const uint16_t *>(k);
+    bp.v = static_cast<const uint16_t *>(v);
+    bp.o = static_cast<const uint16_t *>(o);
+    bp.dout = static_cast<const uint16_t *>(dout);
+    bp.lse = lse;
+    bp.dq = static_cast<uint16_t *>(dq);
+    bp.dk = static_cast<uint16_t *>(dk);
+    bp.dv = static_cast<uint16_t *>(dv);
+    bp.stats = workspace;
+    bp.B = B;
+    bp.H = H;
+    bp.N = N;
+    bp.nqb = (N + 31) / 32;
+    bp.cs = scale * kLog2e;
+    bp.scale = scale;
+    const BwdKernels ks = d == 64 ? select_bwd_d64(causal != 0) : select_bwd_d128(causal != 0);
+    const long long prep_grid = (static_cast<long long>(B) * H * bp.nqb * 32 + 255) / 256;
+    const long long kv_grid = static_cast<long long>(B) * H * ((N + 127) / 128);
+    const long long q_grid = static_cast<long long>(B) * H * ((N + 127) / 128);
+    if (prep_grid > 0x7fffffffLL || kv_grid > 0x7fffffffLL || q_grid > 0x7fffffffLL) return FA_ERR_SHAPE;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(ks.prep, dim3(static_cast<unsigned>(prep_grid)), dim3(256), 0, stream, bp);
+    if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+    hipLaunchKernelGGL(ks.dkdv, dim3(static_cast<unsigned>(kv_grid)), dim3(256), 0, stream, bp);
+    if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+    hipLaunchKernelGGL(ks.dq, dim3(static_cast<unsigned>(q_grid)), dim3(256), 0, stream, bp);
+    if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+    return FA_OK;
+}
+
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
            int d, float scale, int causal, const int32_t *cu_seqlens, hipStream_t stream) {
     return fa_fwd_variant(q, k, v, o, lse, B, H, N, d, scale, causal, cu_seqlens, stream,

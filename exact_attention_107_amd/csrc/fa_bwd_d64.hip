@@ -1,0 +1,8 @@
+// Kernel instances of the attention backward for head dimension 64.
+#include "fa_bwd_kernel.hpp"
+
+namespace fa_detail {
+
+BwdKernels select_bwd_d64(bool causal) { return select_bwd<64>(causal); }
+
+}  // namespace fa_detail

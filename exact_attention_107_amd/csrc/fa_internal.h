@@ -63,4 +63,23 @@ struct MergeParams {
 };
 int launch_merge(const MergeParams &mp, int d, void *stream);
 
+// Backward pass (fa_bwd_kernel.hpp).
+struct BwdParams {
+    const uint16_t *q, *k, *v, *o, *dout;  // bf16 [B, N, H, d]
+    const float *lse;                      // [B, H, N], natural log
+    uint16_t *dq, *dk, *dv;                // bf16 [B, N, H, d]
+    float *stats;                          // [B, H, nqb, 64]: per 32-row block,
+                                           // 32 x LSE*log2(e) then 32 x delta
+    int B, H, N;
+    int nqb;                               // ceil(N / 32)
+    float cs;                              // scale * log2(e)
+    float scale;
+};
+using BwdKernelFn = void (*)(BwdParams);
+struct BwdKernels {
+    BwdKernelFn prep, dkdv, dq;
+};
+BwdKernels select_bwd_d64(bool causal);
+BwdKernels select_bwd_d128(bool causal);
+
 }  // namespace fa_detail

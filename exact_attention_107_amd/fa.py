@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 EXP_HW, EXP_POLY, EXP_MIXED = 0, 1, 2
 RESCALE_ALWAYS, RESCALE_STRICT, RESCALE_THRESHOLD = 0, 1, 2
 EXPORTS = ("fa_fwd", "fa_fwd_variant", "fa_strerror", "fa_tile_rows", "fa_tile_keys",
-           "fa_fwd_splitkv", "fa_merge", "fa_split_range", "fa_num_splits")
+           "fa_fwd_splitkv", "fa_merge", "fa_split_range", "fa_num_splits", "fa_bwd",
+           "fa_bwd_workspace_floats")
 
 _lib = None
 
@@ -61,6 +62,10 @@ def load(path: str | None = None):
     lib.fa_split_range.restype = i32
     lib.fa_num_splits.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.fa_num_splits.restype = i32
+    lib.fa_bwd.argtypes = [vp] * 9 + [i32, i32, i32, i32, ctypes.c_float, i32, vp, vp]
+    lib.fa_bwd.restype = i32
+    lib.fa_bwd_workspace_floats.argtypes = [i32, i32, i32]
+    lib.fa_bwd_workspace_floats.restype = ctypes.c_longlong
     if path is None:
         _lib = lib
     return lib
@@ -251,3 +256,56 @@ def merge(o_part: torch.Tensor, lse_part: torch.Tensor, *, out: torch.Tensor | N
     if rc != 0:
         raise FaError(rc, strerror(rc))
     return out, lse
+
+
+def bwd_workspace_floats(B: int, H: int, N: int) -> int:
+    return int(load().fa_bwd_workspace_floats(int(B), int(H), int(N)))
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+        dout: torch.Tensor, *, causal: bool = False, scale: float | None = None,
+        dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
+        dv: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+        stream: torch.cuda.Stream | None = None):
+    """Gradients of the attention forward (``fa_bwd``), dense ``[B, N, H, d]``.
+
+    ``o`` and ``lse`` are the forward's outputs, ``dout`` the upstream
+    gradient.  Returns ``(dq, dk, dv)`` (bf16, shaped like q); the fp32
+    workspace is allocated with torch unless given.
+    """
+    lib = load()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a GPU tensor")
+    B, N, H, d = _dense_shape(q)
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _check(t, name, torch.bfloat16, dev)
+        if tuple(t.shape) != (B, N, H, d):
+            raise ValueError(f"{name} must be {(B, N, H, d)}")
+    _check(lse, "lse", torch.float32, dev)
+    if tuple(lse.shape) != (B, H, N):
+        raise ValueError(f"lse must be {(B, H, N)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check(t, name, torch.bfloat16, dev)
+        if tuple(t.shape) != (B, N, H, d):
+            raise ValueError(f"{name} must be {(B, N, H, d)}")
+    wf = bwd_workspace_floats(B, H, N)
+    if workspace is None:
+        workspace = torch.empty(wf, dtype=torch.float32, device=dev)
+    _check(workspace, "workspace", torch.float32, dev)
+    if workspace.numel() < wf:
+        raise ValueError(f"workspace needs {wf} floats")
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                        dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
+                        ctypes.c_float(scale), int(bool(causal)), workspace.data_ptr(),
+                        ctypes.c_void_p(s.cuda_stream))
+    if rc != 0:
+        raise FaError(rc, strerror(rc))
+    return dq, dk, dv

@@ -131,6 +131,20 @@ def make_inputs(run: Run, *, B: int | None = None, H: int | None = None,
     }
 
 
+def make_grad(shape, seed: int) -> np.ndarray:
+    """Upstream gradient dO for the backward pass: N(0,1) drawn from its own
+    ``Generator(PCG64(seed))``, rounded once to bf16; returns the bits."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return bf16_bits(rng.standard_normal(size=tuple(shape), dtype=np.float32))
+
+
+def bwd_flops(run_or_lengths, H: int, d: int, causal: bool) -> float:
+    """Credited backward FLOPs: the five n x n x d products of the gradient
+    (S recomputed, dP, dV, dK, dQ) = 10*n^2*d per (sequence, head), halved
+    when causal -- 2.5 times the forward's credit."""
+    return 2.5 * flops(run_or_lengths, H, d, causal)
+
+
 def flops(run_or_lengths, H: int, d: int, causal: bool) -> float:
     """Credited FLOPs: 4*n^2*d per (sequence, head), halved when causal."""
     lengths = np.asarray(run_or_lengths, dtype=np.float64)

@@ -192,6 +192,37 @@ int fa_split_range(int N, int d, int causal, int num_splits, int s, int row,
  * keys long, at most 32. */
 int fa_num_splits(int B, int H, int N, int d, int causal, int num_cus);
 
+/*
+ * fa_bwd: gradients of exact attention (dense layout only, d = 64 or 128).
+ * For the forward O = softmax(scale Q K^T) V and an upstream gradient dO it
+ * writes
+ *     dV = P^T dO,  dQ = scale dS K,  dK = scale dS^T Q,
+ *     dS = P * (dP - delta),  dP = dO V^T,  delta_i = sum_d dO_id O_id,
+ * with P recomputed from the forward's log-sum-exp instead of being stored
+ * (the recomputation of the FlashAttention-1 backward in the summary table
+ * of "FlashAttention 1-4 explained").  No atomics are used: results are
+ * bitwise reproducible run to run (the deterministic mode of section 3.3 of
+ * "Understanding FlashAttention V4").
+ *   q, k, v, o, dout  device bf16 [B, N, H, d]: the forward's inputs, its
+ *                     output O and the upstream gradient dO.
+ *   lse               device fp32 [B, H, N]: the forward's LSE.
+ *   dq, dk, dv        device bf16 outputs [B, N, H, d].
+ *   workspace         device fp32 scratch of fa_bwd_workspace_floats(B, H, N)
+ *                     floats (16-byte aligned); overwritten.
+ *   B, H, N, scale, causal, stream   as fa_fwd.
+ * Three kernels are queued on `stream`.  Outputs and the workspace must not
+ * overlap any input or each other.  Errors as fa_fwd; FA_ERR_HEAD_DIM for
+ * d = 256, which the backward does not support.
+ */
+int fa_bwd(const void *q, const void *k, const void *v, const void *o,
+           const float *lse, const void *dout, void *dq, void *dk, void *dv,
+           int B, int H, int N, int d, float scale, int causal,
+           float *workspace, hipStream_t stream);
+
+/* Size of fa_bwd's workspace in floats: B * H * ceil(N / 32) * 64 (0 for an
+ * invalid shape). */
+long long fa_bwd_workspace_floats(int B, int H, int N);
+
 /* Static, NUL-terminated description of an fa_status code. */
 const char *fa_strerror(int code);
 

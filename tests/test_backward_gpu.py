@@ -1,0 +1,129 @@
+"""Backward pass (fa_bwd), HIP path vs the fp64 oracle of the gradients,
+through the C ABI (needs an MI355X).
+
+The GPU forward's own O and LSE feed the GPU backward, as in training; the
+oracle computes dQ, dK, dV from the definition in fp64.  Errors are measured
+relative to each gradient's scale (the gradients' magnitudes shrink with the
+sequence length, so absolute bounds would not mean the same at every size):
+    rel_rms = ||g - ref||_2 / ||ref||_2,   rel_max = max|g - ref| / max|ref|.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_107_amd import fa
+from exact_attention_107_amd.workloads import RUNS, Run, make_grad, make_inputs
+from gpu_helpers import from_dev, to_dev
+from oracle.backward import attention_backward
+
+pytestmark = pytest.mark.gpu
+
+# bf16 P and dS feed the gradient products and bf16 rounds the outputs
+# (relative 2^-9 each); see the backward section of the design notes.
+GRAD_TOL_RMS = 1e-2
+GRAD_TOL_MAX = 3e-2
+
+
+def _inputs(d, causal, N, B=2, H=3, seed=61, sigma=1.0):
+    inp = make_inputs(Run("bwd", B, H, N, d, causal, seed, sigma_qk=sigma))
+    inp["do"] = make_grad(inp["q"].shape, seed + 5000)
+    return inp
+
+
+def _gpu(inp):
+    q, k, v, do = (to_dev(inp[x]) for x in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, causal=inp["causal"], scale=inp["scale"])
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=inp["causal"], scale=inp["scale"])
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def _grad_metrics(g, ref):
+    diff = np.abs(g - ref)
+    nref = float(np.linalg.norm(ref))
+    return {
+        "rel_rms": float(np.linalg.norm(diff)) / max(nref, 1e-300),
+        "rel_max": float(diff.max()) / max(float(np.abs(ref).max()), 1e-300),
+        "finite": bool(np.all(np.isfinite(g))),
+    }
+
+
+def _check(grads, refs, what):
+    for name, g, ref in zip(("dQ", "dK", "dV"), grads, refs):
+        g = from_dev(g) if isinstance(g, torch.Tensor) else g
+        m = _grad_metrics(g, ref)
+        print(f"{what} {name} {m}")
+        assert m["finite"], f"{what} {name}: non-finite"
+        if not np.any(ref):
+            # exactly zero in exact arithmetic (one key: dS = P (dP - delta)
+            # with dP and delta equal); fp32 leaves a rounding residue
+            assert np.max(np.abs(g)) <= 1e-3, f"{what} {name}: expected zeros, got {np.max(np.abs(g))}"
+            continue
+        assert m["rel_rms"] <= GRAD_TOL_RMS, f"{what} {name}: rel_rms {m['rel_rms']:.3e}"
+        assert m["rel_max"] <= GRAD_TOL_MAX, f"{what} {name}: rel_max {m['rel_max']:.3e}"
+
+
+def _oracle(inp):
+    return attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale=inp["scale"],
+                              causal=inp["causal"])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_small_ragged(d, causal):
+    """Several key tiles and query blocks with ragged tails, every element."""
+    inp = _inputs(d, causal, 300)
+    _check(_gpu(inp), _oracle(inp), f"d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("N", [1, 31, 32, 33, 127, 128, 129, 255, 520])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_edge_lengths(N, causal):
+    inp = _inputs(128, causal, N, B=1, H=2, seed=300 + N)
+    _check(_gpu(inp), _oracle(inp), f"N={N} causal={causal}")
+
+
+def test_bwd_wide_logits():
+    """Scores of a few units (sigma 3 on Q and K): peaked softmax rows."""
+    inp = _inputs(128, False, 400, B=1, H=2, seed=71, sigma=3.0)
+    _check(_gpu(inp), _oracle(inp), "wide logits")
+
+
+def test_bwd_zero_upstream_gradient():
+    inp = _inputs(64, True, 200, B=1, H=2, seed=72)
+    inp["do"] = np.zeros_like(inp["do"])
+    for g in _gpu(inp):
+        assert torch.count_nonzero(g.view(torch.int16)).item() == 0
+
+
+def test_bwd_deterministic():
+    inp = _inputs(128, True, 700, B=1, H=2, seed=73)
+    a = _gpu(inp)
+    b = _gpu(inp)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_bwd_rejects_d256():
+    q = torch.zeros(1, 64, 1, 256, dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros(1, 1, 64, dtype=torch.float32, device="cuda")
+    with pytest.raises(fa.FaError):
+        fa.bwd(q, q.clone(), q.clone(), q.clone(), lse, q.clone())
+
+
+@pytest.mark.parametrize("name", ["mid", "mid_causal"])
+def test_bwd_full_size_sampled_heads(name):
+    """The benchmark's backward shapes at full size; two (b, h) heads are
+    checked in full (each head's gradients depend on that head alone)."""
+    run = RUNS[name]
+    inp = make_inputs(run)
+    inp["do"] = make_grad(inp["q"].shape, run.seed + 5000)
+    dq, dk, dv = _gpu(inp)
+    for b, h in ((0, 0), (run.B - 1, run.H - 1)):
+        sl = {x: inp[x][b:b + 1, :, h:h + 1] for x in ("q", "k", "v", "do")}
+        refs = attention_backward(sl["q"], sl["k"], sl["v"], sl["do"], scale=inp["scale"],
+                                  causal=run.causal)
+        grads = [from_dev(g[b:b + 1, :, h:h + 1]) for g in (dq, dk, dv)]
+        _check(grads, refs, f"{name} b={b} h={h}")
