@@ -24,10 +24,11 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense BF16 flop/clk/CU (the 2.5 PF spec)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fa_fwd_wide.json")
+# Sources that define the forward kernel (the one whose HBM counters are
+# stored): a change to any of them makes the stored traffic stale.
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_107_amd", "csrc", f)
                   for f in ("fa_kernel.hpp", "fa_internal.h", "fa_kernels_d64.hip",
-                            "fa_kernels_d128.hip", "fa_kernels_d256.hip", "fa_merge.hip",
-                            "fa_api.hip")] + \
+                            "fa_kernels_d128.hip", "fa_kernels_d256.hip")] + \
                  [os.path.join(ROOT, "exact_attention_107_amd", "build.py")]
 
 
@@ -157,6 +158,38 @@ def split_kv_runs(torch, fa):
     return res
 
 
+def backward_run(torch, fa, name, steps=10, warmup=2):
+    """fa_bwd (prep, dK/dV and dQ kernels) on one run, after one forward that
+    provides O and LSE.  Credited flops: 10 n^2 d per (sequence, head), halved
+    causal (five n x n x d products); the kernels execute 14 n^2 d (S and dP
+    are recomputed by both the dK/dV and the dQ kernel), which is what the
+    MFMA roofline counts."""
+    from exact_attention_107_amd.workloads import RUNS, bwd_flops, make_grad, make_inputs
+    r = RUNS[name]
+    log(f"[bench] backward run {name}")
+    ri = make_inputs(r)
+    q, k, v = (to_dev(ri[x], torch) for x in ("q", "k", "v"))
+    do = to_dev(make_grad(ri["q"].shape, r.seed + 5000), torch)
+    o, lse = fa.fwd(q, k, v, causal=r.causal, scale=ri["scale"])
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(fa.bwd_workspace_floats(r.B, r.H, r.N), dtype=torch.float32, device="cuda")
+
+    def launch():
+        fa.bwd(q, k, v, o, lse, do, causal=r.causal, scale=ri["scale"], dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    ms_step, ms, ms_med, ms_min = time_launches(launch, steps, warmup, torch)
+    f = bwd_flops(ri["lengths"], r.H, r.d, r.causal)
+    executed = f * 14.0 / 10.0
+    res = {"shape": f"B={r.B} H={r.H} N={r.N} d={r.d} causal={r.causal}", "ms": round(ms, 4),
+           "ms_per_step": round(ms_step, 4), "tflops_credited": round(f / ms / 1e9, 1),
+           "roofline": {"bound": "mfma", "achieved": round(executed / ms / 1e9, 1), "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(executed / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                        "per_launch": "14*B*H*N^2*d executed MFMA flops (halved causal) / mean HIP-event "
+                                      "duration of the three backward kernels"}}
+    del q, k, v, do, o, lse, dq, dk, dv, ws
+    return res, f, ms_step
+
+
 def traffic_for(fingerprint: str):
     try:
         with open(TRAFFIC_FILE) as f:
@@ -177,6 +210,8 @@ def main() -> int:
     ap.add_argument("--extra", type=int, default=1, help="also time the other runs and variants")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+                    help="bwd: time only the backward pass of --workload (for profiling)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "
                          "reference dispatch for HBM byte counters)")
@@ -196,6 +231,16 @@ def main() -> int:
         return 2
     fa.load()
     props = torch.cuda.get_device_properties(0)
+    if args.which == "bwd":
+        res, f, ms_step = backward_run(torch, fa, args.workload, args.steps, args.warmup)
+        print(json.dumps({
+            "metric": "attention bwd TFLOP/s (bf16, credited 10*B*H*N^2*d, halved causal)",
+            "value": res["tflops_credited"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"{args.workload}: {res['shape']}"}, "roofline": res["roofline"],
+            "kernel_fingerprint": kernel_fingerprint()}), flush=True)
+        return 0
     run = RUNS[args.workload]
     log(f"[bench] generating {run.name} inputs")
     inp = make_inputs(run)
@@ -282,6 +327,8 @@ def main() -> int:
                                           "tflops": round(f / (kms * 1e-3) / 1e12, 1)}
         out["variants"] = variants
         out["split_kv"] = split_kv_runs(torch, fa)
+        out["backward"] = {name: backward_run(torch, fa, name)[0]
+                           for name in ("mid", "mid_causal", "bwd_long", "bwd_long_causal")}
 
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")

@@ -69,6 +69,9 @@ RUNS = {
     # the GPU, the shape the split of the key sequence is for
     "few_heads": Run("few_heads", 1, 4, 8192, 128, False, 1006),
     "few_heads_causal": Run("few_heads_causal", 1, 4, 16384, 128, True, 1007),
+    # backward pass at the forward's long shape, N(0,1) inputs
+    "bwd_long": Run("bwd_long", 2, 16, 8192, 128, False, 1008),
+    "bwd_long_causal": Run("bwd_long_causal", 2, 16, 8192, 128, True, 1008),
 }
 
 
