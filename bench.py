@@ -204,8 +204,8 @@ def traffic_for(fingerprint: str):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="wide")
     ap.add_argument("--extra", type=int, default=1, help="also time the other runs and variants")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)

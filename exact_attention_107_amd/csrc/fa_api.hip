@@ -109,7 +109,7 @@ int fa_fwd_variant(const void *q, const void *k, const void *v, void *o, float *
 
     KernelFn fn = pick(d, causal != 0, varlen, exp_mode, rescale_mode);
     (void)hipGetLastError();  // clear a stale error so the check below is ours
-    hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(grid)), dim3(kWorkgroupWaves * 64), 0, stream, prm);
+    hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(grid)), dim3(waves_for(d) * 64), 0, stream, prm);
     if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
     return FA_OK;
 }
@@ -133,9 +133,9 @@ int fa_split_range(int N, int d, int causal, int num_splits, int s, int row, int
 int fa_num_splits(int B, int H, int N, int d, int causal, int num_cus) {
     if (B < 1 || H < 1 || N < 1 || tile_rows_for(d) == 0) return 1;
     const long long cus = num_cus > 0 ? num_cus : 256;
-    // workgroups resident per compute unit (LDS and registers): 3, 2, 1
-    const long long per_cu = d == 64 ? 3 : (d == 128 ? 2 : 1);
-    const long long slots = per_cu * cus;
+    // workgroups resident per compute unit (registers): 3, 1, 1 at d = 64,
+    // 128, 256
+    const long long slots = static_cast<long long>(resident_for(d)) * cus;
     const long long n_qt = (static_cast<long long>(N) + tile_rows_for(d) - 1) / tile_rows_for(d);
     // causal: the average query tile sees half the keys
     const long long wgs = static_cast<long long>(B) * H * n_qt / (causal ? 2 : 1);
@@ -233,7 +233,7 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
         default: fn = select_split_d256(causal != 0); break;
     }
     (void)hipGetLastError();
-    hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(grid)), dim3(kWorkgroupWaves * 64), 0, stream, prm);
+    hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(grid)), dim3(waves_for(d) * 64), 0, stream, prm);
     if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
 
     MergeParams mp;

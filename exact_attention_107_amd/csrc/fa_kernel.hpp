@@ -861,7 +861,7 @@ fa_fwd_kernel(Params p) {
 
 template <int D, bool CAUSAL, bool VARLEN, int EXPM>
 KernelFn select_rsm(int rsm) {
-    constexpr int BC = kTileKeys, NW = kWorkgroupWaves, QB = Geometry<D>::kBlocks;
+    constexpr int BC = kTileKeys, NW = Geometry<D>::kWaves, QB = Geometry<D>::kBlocks;
     switch (rsm) {
         case FA_RESCALE_ALWAYS: return fa_fwd_kernel<D, BC, NW, QB, CAUSAL, VARLEN, EXPM, FA_RESCALE_ALWAYS>;
         case FA_RESCALE_STRICT: return fa_fwd_kernel<D, BC, NW, QB, CAUSAL, VARLEN, EXPM, FA_RESCALE_STRICT>;
@@ -880,7 +880,7 @@ KernelFn select_exp(int expm, int rsm) {
 
 template <int D>
 KernelFn select_split(bool causal) {
-    constexpr int BC = kTileKeys, NW = kWorkgroupWaves, QB = Geometry<D>::kBlocks;
+    constexpr int BC = kTileKeys, NW = Geometry<D>::kWaves, QB = Geometry<D>::kBlocks;
     if (causal) return fa_fwd_kernel<D, BC, NW, QB, true, false, FA_EXP_HW, FA_RESCALE_THRESHOLD, true>;
     return fa_fwd_kernel<D, BC, NW, QB, false, false, FA_EXP_HW, FA_RESCALE_THRESHOLD, true>;
 }

@@ -186,7 +186,7 @@ int fa_split_range(int N, int d, int causal, int num_splits, int s, int row,
 
 /* A split count for fa_fwd_splitkv on a GPU with num_cus compute units
  * (<= 0: 256).  Returns 1 (use fa_fwd) when fa_fwd's workgroups (counted
- * half when causal) already fill every resident slot (3, 2 or 1 workgroups
+ * half when causal) already fill every resident slot (3, 1 or 1 workgroups
  * per compute unit at d = 64, 128, 256), or fill one per compute unit and
  * N < 8192; otherwise enough ranges to fill the slots, each at least 1024
  * keys long, at most 32. */

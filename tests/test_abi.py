@@ -149,9 +149,10 @@ def test_split_range(lib):
     assert fa.split_range(1000, 128, False, 4, 0, 5) == (0, 256)
     assert fa.split_range(1000, 128, False, 4, 3, 999) == (768, 1000)
     assert fa.split_range(1000, 128, False, 3, 1, 0) == (320, 640)
-    # causal: the tile of rows 128..255 sees keys < 256 (4 tiles)
-    assert fa.split_range(1000, 128, True, 2, 0, 130) == (0, 128)
-    assert fa.split_range(1000, 128, True, 2, 1, 255) == (128, 256)
+    # causal: a query tile of fa_tile_rows(d) rows sees the keys up to its last row
+    rows = fa.tile_rows(128)
+    assert fa.split_range(1000, 128, True, 2, 0, rows + 2) == (0, rows)
+    assert fa.split_range(1000, 128, True, 2, 1, 2 * rows - 1) == (rows, 2 * rows)
     # the last tile sees up to N
     assert fa.split_range(1000, 128, True, 2, 1, 999) == (512, 1000)
     for N in (1, 63, 64, 65, 1000, 8191):
@@ -159,7 +160,8 @@ def test_split_range(lib):
         for causal in (False, True):
             for S in range(1, min(tiles, 20) + 1):
                 for row in sorted({0, N // 3, N - 1}):
-                    seen = min(N, (row // 128 + 1) * 128) if causal else N
+                    rows = fa.tile_rows(128)
+                    seen = min(N, (row // rows + 1) * rows) if causal else N
                     ranges = [fa.split_range(N, 128, causal, S, s, row) for s in range(S)]
                     # consecutive, tile-aligned, covering [0, seen), near-equal
                     assert ranges[0][0] == 0 and ranges[-1][1] == seen, (N, S, row, ranges)
@@ -179,9 +181,12 @@ def test_num_splits_heuristic(lib):
     assert fa.num_splits(2, 16, 8192, 128, False, 256) == 1
     # one head of 8192 keys: 64 query tiles for 512 slots -> 8 ranges of 1024 keys
     assert fa.num_splits(1, 1, 8192, 128, False, 256) == 8
-    # one workgroup per CU already: split only long sequences
+    # d = 128 workgroups are 256 rows, one per CU: half the CUs idle -> split
     assert fa.num_splits(1, 4, 8192, 128, False, 256) == 2
-    assert fa.num_splits(1, 8, 4096, 128, False, 256) == 1
+    assert fa.num_splits(1, 8, 4096, 128, False, 256) == 2
+    # one workgroup per CU already (d = 64 fits three): split only long sequences
+    assert fa.num_splits(1, 8, 4096, 64, False, 256) == 1
+    assert fa.num_splits(1, 8, 8192, 64, False, 256) == 2
     # ranges of at least 1024 keys
     assert fa.num_splits(1, 1, 512, 128, False, 256) == 1
     assert fa.num_splits(1, 1, 2048, 128, False, 256) == 2
