@@ -1,0 +1,126 @@
+"""The FP8 side of the oracle (E4M3 decode/encode, per-head quantisation,
+attention of dequantised inputs) against facts it does not derive itself:
+the values the OCP E4M3 definition fixes, torch's float8_e4m3fn conversion
+(an independent library route), round trips, and the C oracle on inputs that
+are exact in bf16."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import fp8
+from exact_attention_107_amd.workloads import bf16_bits, bf16_to_f32
+
+
+def test_decode_fixed_values():
+    spec = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0, 0x39: 1.125,
+            0x3f: 1.875, 0x40: 2.0, 0x77: 240.0, 0x78: 256.0, 0x7e: 448.0, 0x80: -0.0, 0xb8: -1.0,
+            0xfe: -448.0}
+    for c, v in spec.items():
+        got = fp8.e4m3_decode(np.uint8(c))
+        assert got == v and np.signbit(got) == np.signbit(v), (hex(c), got, v)
+    assert np.isnan(fp8.e4m3_decode(np.uint8(0x7f))) and np.isnan(fp8.e4m3_decode(np.uint8(0xff)))
+
+
+def test_decode_matches_torch_for_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = fp8.e4m3_decode(codes)
+    both_nan = np.isnan(ref) & np.isnan(got)
+    assert np.all(both_nan | (ref == got))
+
+
+def test_encode_round_trip_and_ties():
+    codes = np.array([c for c in range(256) if c & 0x7f != 0x7f], dtype=np.uint8)
+    assert np.array_equal(fp8.e4m3_encode(fp8.e4m3_decode(codes)), codes)
+    # midpoints between neighbours go to the code with an even mantissa
+    pos = np.arange(0x7e, dtype=np.uint8)
+    lo, hi = fp8.e4m3_decode(pos), fp8.e4m3_decode(pos + 1)
+    mid = (lo + hi) / 2
+    want = np.where(pos % 2 == 0, pos, pos + 1).astype(np.uint8)
+    assert np.array_equal(fp8.e4m3_encode(mid), want)
+    assert np.array_equal(fp8.e4m3_encode(-mid), want | 0x80)
+    with pytest.raises(ValueError):
+        fp8.e4m3_encode(np.array([449.0]))
+
+
+def test_encode_matches_torch_on_random_values():
+    rng = np.random.Generator(np.random.PCG64(5))
+    x = np.concatenate([rng.uniform(-448, 448, 20000), rng.standard_normal(20000) * 0.01,
+                        rng.standard_normal(20000)]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(fp8.e4m3_encode(x.astype(np.float64)), ref)
+
+
+def test_quantize_per_head():
+    rng = np.random.Generator(np.random.PCG64(6))
+    x = bf16_bits((rng.standard_normal((2, 50, 3, 16)) * np.array([1, 10, 0.1])[None, None, :, None])
+                  .astype(np.float32))
+    x[1, :, 2, :] = 0  # an all-zero head
+    codes, ds = fp8.quantize(x)
+    xf = bf16_to_f32(x).astype(np.float64)
+    deq = fp8.e4m3_decode(codes) * ds[:, None, :, None]
+    for b in range(2):
+        for h in range(3):
+            amax = np.abs(xf[b, :, h]).max()
+            if amax == 0:
+                assert ds[b, h] == 1.0 and np.all(codes[b, :, h] == 0)
+                continue
+            assert np.isclose(ds[b, h], amax / 448, rtol=1e-6)
+            assert np.max(np.abs(fp8.e4m3_decode(codes[b, :, h]))) == 448.0
+            # relative rounding error of E4M3 normals <= 2^-4 (plus subnormal spacing)
+            err = np.abs(deq[b, :, h] - xf[b, :, h])
+            bound = np.maximum(np.abs(xf[b, :, h]) * 2.0 ** -4, 2.0 ** -10 * ds[b, h])
+            assert np.all(err <= bound * (1 + 1e-6))
+    ct, dt = fp8.quantize(x, transpose=True)
+    assert np.array_equal(ct, codes.transpose(0, 2, 3, 1)) and np.array_equal(dt, ds)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_matches_c_oracle_on_exact_inputs(causal, oracle_lib):
+    """E4M3 values times power-of-two descales are exact in bf16, so the FP8
+    attention must equal the C oracle's attention of those bf16 values."""
+    rng = np.random.Generator(np.random.PCG64(7))
+    B, N, H, d = 2, 37, 2, 32
+    q8, k8, v8 = (rng.integers(0, 256, (B, N, H, d)).astype(np.uint8) for _ in range(3))
+    for a in (q8, k8, v8):
+        a[(a & 0x7f) == 0x7f] = 0x38  # no NaN codes
+        a[(a & 0x78) == 0x78] = 0x40  # keep magnitudes <= 240 so that scores stay moderate
+    dq = np.array([[2.0 ** -4, 2.0 ** -5], [2.0 ** -3, 2.0 ** -4]], np.float32)
+    dk = np.array([[2.0 ** -4, 2.0 ** -6], [2.0 ** -5, 2.0 ** -4]], np.float32)
+    dv = np.array([[1.0, 0.5], [0.25, 2.0]], np.float32)
+    vt8 = np.ascontiguousarray(v8.transpose(0, 2, 3, 1))
+    o, lse = fp8.attention(q8, k8, vt8, dq, dk, dv, scale=0.125, causal=causal)
+    deq = lambda c, s: bf16_bits((fp8.e4m3_decode(c) * s[:, None, :, None]).astype(np.float32))
+    ro, rl = oracle.attention(deq(q8, dq), deq(k8, dk), deq(v8, dv), scale=0.125, causal=causal,
+                              lib=oracle_lib)
+    assert np.max(np.abs(o - ro)) <= 1e-12 * max(1.0, np.abs(ro).max())
+    assert np.max(np.abs(lse - rl)) <= 1e-10
+    rows = np.array([[0, 0, 0], [1, 1, 36], [0, 1, 17]])
+    orow, lrow = fp8.attention(q8, k8, vt8, dq, dk, dv, scale=0.125, causal=causal, rows=rows)
+    assert np.allclose(orow, o[rows[:, 0], rows[:, 2], rows[:, 1]], rtol=0, atol=1e-12)
+    assert np.allclose(lrow, lse[rows[:, 0], rows[:, 1], rows[:, 2]], rtol=0, atol=1e-12)
+
+
+def test_planted_mistakes_are_caught(monkeypatch, oracle_lib):
+    """Broken copies of the FP8 helpers fail the tests above."""
+    good_decode = fp8.e4m3_decode
+    monkeypatch.setattr(fp8, "e4m3_decode", lambda c: good_decode(c) * 2.0)  # bias 6
+    with pytest.raises(AssertionError):
+        test_decode_fixed_values()
+    monkeypatch.setattr(fp8, "e4m3_decode", good_decode)
+    good_encode = fp8.e4m3_encode
+    # ties away from zero instead of to even
+    def away(x):
+        x = np.asarray(x, np.float64)
+        return good_encode(np.clip(x + np.sign(x) * 1e-12 * np.maximum(np.abs(x), 2.0 ** -9), -448, 448))
+    monkeypatch.setattr(fp8, "e4m3_encode", away)
+    with pytest.raises(AssertionError):
+        test_encode_round_trip_and_ties()
+    monkeypatch.setattr(fp8, "e4m3_encode", good_encode)
+    good_attention = fp8.attention
+    # descale of V dropped
+    monkeypatch.setattr(fp8, "attention",
+                        lambda q8, k8, vt8, dq, dk, dv, **kw: good_attention(q8, k8, vt8, dq, dk, np.ones_like(dv), **kw))
+    with pytest.raises(AssertionError):
+        test_attention_matches_c_oracle_on_exact_inputs(False, oracle_lib)
