@@ -12,9 +12,11 @@ readings taken here:
   infinities, code 0x7f / 0xff is NaN, largest finite 448.
 * Scaling is per (sequence, head): x = code_value * descale, with
   descale = amax / 448 over that head's values (amax = 0 gives descale 1 and
-  all-zero codes).  Codes are x * (448 / amax) rounded to nearest, ties to
-  even, computed in fp32 -- the quantisation decision is taken in the
+  all-zero codes).  Codes are x * (1 / descale) rounded to nearest, ties to
+  even, every step in fp32 -- the quantisation decision is taken in the
   precision the kernel takes it in.
+* V is also offered transposed, [B, H, d, Np] with rows padded by zero codes
+  to Np = ceil(N / 64) * 64 (the layout the FP8 kernel reads).
 * The attention of the FP8 inputs is the exact attention of the dequantised
   values (code value times descale, exact in fp64).
 """
@@ -63,28 +65,33 @@ def e4m3_encode(x) -> np.ndarray:
 def quantize(x_bits, *, transpose: bool = False):
     """Per-(b, h) E4M3 quantisation of a bf16 ``[B, N, H, d]`` tensor.
 
-    Returns ``(codes, descale)``: codes ``[B, N, H, d]`` (or ``[B, H, d, N]``
-    when ``transpose``) and descale ``[B, H]`` fp32 (= amax / 448).
+    Returns ``(codes, descale)``: codes ``[B, N, H, d]``, or when
+    ``transpose`` ``[B, H, d, Np]`` with ``Np = ceil(N / 64) * 64`` and zero
+    codes in the padding; descale ``[B, H]`` fp32 (= amax / 448).
     """
     x = (np.asarray(x_bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
     B, N, H, d = x.shape
     amax = np.max(np.abs(x), axis=(1, 3)).astype(np.float32)        # [B, H]
     safe = np.where(amax > 0, amax, np.float32(E4M3_MAX)).astype(np.float32)
-    inv = (np.float32(E4M3_MAX) / safe).astype(np.float32)          # fp32 division
     descale = np.where(amax > 0, (safe / np.float32(E4M3_MAX)).astype(np.float32),
-                       np.float32(1.0)).astype(np.float32)
+                       np.float32(1.0)).astype(np.float32)         # fp32 division
+    inv = (np.float32(1.0) / descale).astype(np.float32)             # fp32 reciprocal
     y = (x * inv[:, None, :, None]).astype(np.float32)              # fp32 product
     y = np.clip(y, -E4M3_MAX, E4M3_MAX)                             # |y| <= 448 up to rounding
     codes = e4m3_encode(y)
     if transpose:
-        codes = np.ascontiguousarray(codes.transpose(0, 2, 3, 1))
+        np_ = (N + 63) // 64 * 64
+        t = np.zeros((B, H, d, np_), dtype=np.uint8)
+        t[..., :N] = codes.transpose(0, 2, 3, 1)
+        codes = t
     return codes, descale
 
 
 def attention(q8, k8, vt8, dq, dk, dv, *, scale: float, causal: bool, rows=None):
     """Exact attention (fp64) of dequantised E4M3 inputs.
 
-    q8, k8  ``[B, N, H, d]`` codes; vt8 ``[B, H, d, N]`` codes (V transposed);
+    q8, k8  ``[B, N, H, d]`` codes; vt8 ``[B, H, d, >= N]`` codes (V
+            transposed; columns past N are ignored);
     dq, dk, dv  ``[B, H]`` descales; rows None (all) or ``(n, 3)`` (b, h, i).
     Returns ``(o, lse)``: ``o [B, N, H, d]`` and ``lse [B, H, N]`` for all
     rows, else ``o [n, d]`` and ``lse [n]``.
@@ -92,7 +99,7 @@ def attention(q8, k8, vt8, dq, dk, dv, *, scale: float, causal: bool, rows=None)
     B, N, H, d = q8.shape
     Q = e4m3_decode(q8) * np.asarray(dq, np.float64)[:, None, :, None]
     K = e4m3_decode(k8) * np.asarray(dk, np.float64)[:, None, :, None]
-    Vt = e4m3_decode(vt8) * np.asarray(dv, np.float64)[:, :, None, None]   # [B, H, d, N]
+    Vt = e4m3_decode(vt8[..., :N]) * np.asarray(dv, np.float64)[:, :, None, None]   # [B, H, d, N]
     sc = float(np.float32(scale))
     full = rows is None
     if full:

@@ -73,7 +73,8 @@ def test_quantize_per_head():
             bound = np.maximum(np.abs(xf[b, :, h]) * 2.0 ** -4, 2.0 ** -10 * ds[b, h])
             assert np.all(err <= bound * (1 + 1e-6))
     ct, dt = fp8.quantize(x, transpose=True)
-    assert np.array_equal(ct, codes.transpose(0, 2, 3, 1)) and np.array_equal(dt, ds)
+    assert ct.shape == (2, 3, 16, 64) and np.all(ct[..., 50:] == 0)
+    assert np.array_equal(ct[..., :50], codes.transpose(0, 2, 3, 1)) and np.array_equal(dt, ds)
 
 
 @pytest.mark.parametrize("causal", [False, True])
