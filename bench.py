@@ -190,6 +190,45 @@ def backward_run(torch, fa, name, steps=10, warmup=2):
     return res, f, ms_step
 
 
+PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS  # dense E4M3 MFMA rate is twice BF16's
+
+
+def fp8_runs(torch, fa):
+    """FP8 (E4M3) forward on the headline shape and two others: inputs are
+    quantised per head once, outside the timed launches; the quantisation of
+    one tensor is timed on its own."""
+    from exact_attention_107_amd.workloads import RUNS, flops, make_inputs
+    res = {}
+    for name in ("wide", "long_causal", "mid"):
+        r = RUNS[name]
+        log(f"[bench] fp8 run {name}")
+        ri = make_inputs(r)
+        q, k, v = (to_dev(ri[x], torch) for x in ("q", "k", "v"))
+        q8, dq = fa.quantize_fp8(q)
+        k8, dk = fa.quantize_fp8(k)
+        vt8, dv = fa.quantize_fp8(v, transpose=True)
+        o = torch.empty_like(q)
+        lse = torch.empty((r.B, r.H, r.N), dtype=torch.float32, device="cuda")
+        f = flops(ri["lengths"], r.H, r.d, r.causal)
+
+        def launch():
+            fa.fwd_fp8(q8, k8, vt8, dq, dk, dv, causal=r.causal, scale=ri["scale"], out=o, lse=lse)
+
+        def quant():
+            fa.quantize_fp8(q, out=q8, descale=dq)
+
+        _, ms, _, _ = time_launches(launch, 30, 30, torch)
+        _, msq, _, _ = time_launches(quant, 10, 3, torch)
+        tf = f / ms / 1e9
+        res[name] = {"shape": f"B={r.B} H={r.H} N={r.N} d={r.d} causal={r.causal}", "ms": round(ms, 4),
+                     "tflops": round(tf, 1),
+                     "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_FP8_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4)},
+                     "quantize_one_tensor_ms": round(msq, 4)}
+        del q, k, v, q8, k8, vt8, o, lse
+    return res
+
+
 def traffic_for(fingerprint: str):
     try:
         with open(TRAFFIC_FILE) as f:
@@ -329,6 +368,7 @@ def main() -> int:
         out["split_kv"] = split_kv_runs(torch, fa)
         out["backward"] = {name: backward_run(torch, fa, name)[0]
                            for name in ("mid", "mid_causal", "bwd_long", "bwd_long_causal")}
+        out["fp8"] = fp8_runs(torch, fa)
 
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")

@@ -33,11 +33,13 @@ UNITS = [
     ("fa_kernels_d256.hip", []),
     ("fa_bwd_d64.hip", VGPR_FORM),
     ("fa_bwd_d128.hip", VGPR_FORM),
+    ("fa_fp8.hip", []),
     ("fa_merge.hip", []),
     ("fa_api.hip", []),
 ]
 SOURCES = [os.path.join(CSRC, u) for u, _ in UNITS] + [os.path.join(CSRC, "fa_kernel.hpp"),
                                                        os.path.join(CSRC, "fa_bwd_kernel.hpp"),
+                                                       os.path.join(CSRC, "fa_fp8_kernel.hpp"),
                                                        os.path.join(CSRC, "fa_internal.h")]
 
 

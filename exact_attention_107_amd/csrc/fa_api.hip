@@ -314,6 +314,80 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const flo
     return FA_OK;
 }
 
+int fa_fp8_vt_stride(int N) { return N < 1 ? 0 : (N + 63) / 64 * 64; }
+
+int fa_quantize_fp8(const void *x, void *x8, float *descale, int B, int H, int N, int d, int transpose,
+                    hipStream_t stream) {
+    if (!x || !x8 || !descale) return FA_ERR_NULLPTR;
+    if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128 && d != 256) return FA_ERR_HEAD_DIM;
+    if (misaligned(x, 16) || misaligned(x8, 4) || misaligned(descale, 4)) return FA_ERR_ALIGN;
+    const long long tokens = transpose ? fa_fp8_vt_stride(N) : N;
+    const long long elems = static_cast<long long>(B) * H * tokens * d;
+    if (elems <= 0 || elems > (1LL << 46) || !token_stride_ok(H, d)) return FA_ERR_SHAPE;
+    const size_t xb = static_cast<size_t>(B) * N * H * d * 2, x8b = static_cast<size_t>(elems);
+    const size_t db = static_cast<size_t>(B) * H * 4;
+    if (overlap(x8, x8b, x, xb) || overlap(descale, db, x, xb) || overlap(descale, db, x8, x8b)) return FA_ERR_ALIAS;
+    QuantParams qp;
+    qp.x = static_cast<const uint16_t *>(x);
+    qp.x8 = static_cast<uint8_t *>(x8);
+    qp.descale = descale;
+    qp.B = B;
+    qp.H = H;
+    qp.N = N;
+    qp.d = d;
+    qp.transpose = transpose != 0;
+    (void)hipGetLastError();
+    return launch_quant(qp, stream) == 0 ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_fp8(const void *q8, const void *k8, const void *vt8, const float *descale_q, const float *descale_k,
+               const float *descale_v, void *o, float *lse, int B, int H, int N, int d, float scale, int causal,
+               hipStream_t stream) {
+    if (!q8 || !k8 || !vt8 || !descale_q || !descale_k || !descale_v || !o || !lse) return FA_ERR_NULLPTR;
+    if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+    if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_SCALE;
+    if (misaligned(q8, 16) || misaligned(k8, 16) || misaligned(vt8, 16) || misaligned(o, 16) ||
+        misaligned(lse, 4) || misaligned(descale_q, 4) || misaligned(descale_k, 4) || misaligned(descale_v, 4))
+        return FA_ERR_ALIGN;
+    const long long rows = static_cast<long long>(B) * N * H;
+    const long long elems = rows * d;
+    const long long vt_elems = static_cast<long long>(B) * H * d * fa_fp8_vt_stride(N);
+    if (elems <= 0 || elems > (1LL << 46) || !token_stride_ok(H, d) ||
+        static_cast<long long>(d) * fa_fp8_vt_stride(N) > 0x7fffffffLL)
+        return FA_ERR_SHAPE;
+    const size_t qb = static_cast<size_t>(elems), vb = static_cast<size_t>(vt_elems);
+    const size_t ob = static_cast<size_t>(elems) * 2, lb = static_cast<size_t>(rows) * 4;
+    const size_t sb = static_cast<size_t>(B) * H * 4;
+    const void *ins[] = {q8, k8, vt8, descale_q, descale_k, descale_v};
+    const size_t in_bytes[] = {qb, qb, vb, sb, sb, sb};
+    for (int i = 0; i < 6; ++i)
+        if (overlap(o, ob, ins[i], in_bytes[i]) || overlap(lse, lb, ins[i], in_bytes[i])) return FA_ERR_ALIAS;
+    if (overlap(o, ob, lse, lb)) return FA_ERR_ALIAS;
+
+    Fp8Params fp;
+    fp.q = static_cast<const uint8_t *>(q8);
+    fp.k = static_cast<const uint8_t *>(k8);
+    fp.vt = static_cast<const uint8_t *>(vt8);
+    fp.dq = descale_q;
+    fp.dk = descale_k;
+    fp.dv = descale_v;
+    fp.o = static_cast<uint16_t *>(o);
+    fp.lse = lse;
+    fp.B = B;
+    fp.H = H;
+    fp.N = N;
+    fp.cs = scale * kLog2e;
+    const long long n_qt = (static_cast<long long>(N) + kFp8Rows - 1) / kFp8Rows;
+    const long long grid = static_cast<long long>(B) * H * n_qt;
+    if (grid <= 0 || grid > 0x7fffffffLL) return FA_ERR_SHAPE;
+    const KernelFp8Fn fn = d == 64 ? select_fp8_d64(causal != 0) : select_fp8_d128(causal != 0);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(grid)), dim3(kFp8Rows * 2), 0, stream, fp);
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
            int d, float scale, int causal, const int32_t *cu_seqlens, hipStream_t stream) {
     return fa_fwd_variant(q, k, v, o, lse, B, H, N, d, scale, causal, cu_seqlens, stream,

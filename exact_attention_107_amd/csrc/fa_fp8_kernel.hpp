@@ -1,0 +1,352 @@
+// Device code of the FP8 (E4M3) attention forward for gfx950 and of the
+// per-head E4M3 quantisation that feeds it (fa_fp8.hip).
+//
+// The FlashAttention-3 notes of "FlashAttention 1-4 explained" run the
+// forward's two products on FP8 matrix units; here both run as
+// v_mfma_f32_32x32x64_f8f6f4 with E4M3 operands and fp32 accumulation:
+//  * S^T = K Q^T per 32-key block and 64-wide k step: K (A operand) from LDS,
+//    each lane reading 32 consecutive bytes of its key's row; Q (B operand)
+//    held in VGPRs for the whole kernel.  Each lane again owns one query row.
+//  * P = 2^(s c - m) (strict rescale: m is the running row max, so P <= 1) is
+//    scaled by 2^8 and rounded to E4M3 (v_cvt_pk_fp8_f32, nearest even): the
+//    scale keeps values down to 2^-18 of the row max out of the flush-to-zero
+//    range, and 2^8 P <= 256 stays below the E4M3 maximum 448.  The row sum l
+//    is accumulated from the fp32 P.
+//  * O^T += V^T P^T takes P as the B operand, whose 64 keys must sit as 32
+//    consecutive keys per lane half.  The accumulator gives lane half hh the
+//    keys 8g + 4hh + r of both 32-key blocks; one v_permlane32_swap per
+//    register pair moves block 0's keys to the lower half and block 1's to
+//    the upper half, after which packing four keys per register is exactly
+//    the operand order.  V is read from a transposed copy (V^T,
+//    [B, H, d, Np] with rows padded with zero codes to Np = ceil(N/64)*64) so
+//    that its A operand is again 32 consecutive bytes of one LDS row.
+//  * Scores are scaled by scale * descale_q * descale_k (folded into c) and
+//    the output by descale_v / (2^8 l).
+// LDS rows are 64 or 128 bytes; their 16-byte chunks are XOR-permuted so
+// that the 16 rows of one fragment read cover 16 distinct bank groups.
+
+#pragma once
+
+#include "fa_kernel.hpp"
+
+namespace fa_detail {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kFp8Waves = kFp8Rows / 32;
+constexpr int kFp8Keys = 64;            // keys per K / V^T tile
+constexpr float kFp8PScale = 256.0f;    // P is stored as E4M3(2^8 P)
+
+// chunk permutation of row r for rows of RB bytes (RB = 64 or 128)
+template <int RB>
+__device__ __forceinline__ int fp8_swz(int r) {
+    if constexpr (RB == 128) return (r >> 1) & 7;  // 2 rows per 256-byte bank window
+    else return (r >> 2) & 3;                      // 4 rows per window
+}
+
+// 4 E4M3 codes of a, b, c, d (nearest even; |x| <= 448 required)
+__device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
+    int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+}
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(kFp8Waves * 64) fa_fp8_fwd_kernel(Fp8Params p) {
+    constexpr int NW = kFp8Waves, BC = kFp8Keys, BR = NW * 32;
+    constexpr int KS = D / 64;          // 64-wide k steps of Q K^T
+    constexpr int NDB = D / 32;         // 32-wide d blocks of O^T
+    constexpr int KRB = D;              // bytes per K row
+    constexpr int VRB = BC;             // bytes per V^T row (64 keys)
+    constexpr int KT = BC * KRB;        // bytes of a K tile
+    constexpr int VT = D * VRB;         // bytes of a V^T tile
+    constexpr int KBLK = KT / 1024, VBLK = VT / 1024;
+    static_assert(KBLK % NW == 0 && VBLK % NW == 0, "tiles must split over the waves");
+
+    __shared__ __attribute__((aligned(1024))) char k_lds0[KT], k_lds1[KT], v_lds0[VT], v_lds1[VT];
+
+    const int BH = p.B * p.H;
+    const int n = p.N;
+    const int n_qt = (n + BR - 1) / BR;
+    int bh, qt;
+    if constexpr (CAUSAL) {
+        qt = n_qt - 1 - static_cast<int>(blockIdx.x) / BH;  // longest first
+        bh = blockIdx.x - (n_qt - 1 - qt) * BH;
+    } else {
+        const int G = gridDim.x, x = blockIdx.x & 7, sx = blockIdx.x >> 3;
+        const int per = G >> 3, rem = G & 7;
+        const int item = x * per + (x < rem ? x : rem) + sx;
+        bh = item / n_qt;
+        qt = item - bh * n_qt;
+    }
+    const int b = bh / p.H, h = bh - b * p.H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane & 31, hh = lane >> 5;
+    const int q0 = qt * BR;
+    const int wrow0 = q0 + wave * 32;
+    const int rs = p.H * D;                                   // token stride of q8, k8 (bytes)
+    const long long base8 = (static_cast<long long>(b) * n * p.H + h) * D;
+    const int np = (n + 63) / 64 * 64;                        // V^T row stride (bytes)
+    const uint8_t *vt = p.vt + static_cast<long long>(bh) * D * np;  // V^T rows of (b, h)
+
+    // per-(b, h) scales: scores by scale * dq * dk (log2 units), output by dv
+    const float cs = p.cs * p.dq[bh] * p.dk[bh];
+    const float dv = p.dv[bh];
+
+    // Q of this wave's rows, B operand: lane (c, hh) holds bytes
+    // 64 ks + 32 hh .. +32 of row wrow0 + c
+    i32x8 qf[KS];
+    {
+        const auto qrs = make_rsrc(p.q + base8 + static_cast<long long>(wrow0) * rs, (long long)(n - wrow0) * rs);
+        const int vo = c * rs + hh * 32;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(qrs, vo + ks * 64, 0, 0);
+            const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(qrs, vo + ks * 64 + 16, 0, 0);
+            qf[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+    }
+
+    // direct loads: lane l of 1 KB load I fills row r = (1024 I + 16 l) / RB,
+    // physical chunk pc, with logical chunk pc ^ swz(r); swz depends on I only
+    // through I mod NW here, so one per-lane offset serves a wave's loads
+    int kvo, vvo;
+    {
+        const int pos = wave * 1024 + lane * 16;
+        const int kr = pos / KRB, kpc = (pos % KRB) / 16;
+        kvo = kr * rs + ((kpc ^ fp8_swz<KRB>(kr)) << 4);
+        const int vr = pos / VRB, vpc = (pos % VRB) / 16;
+        vvo = vr * np + ((vpc ^ fp8_swz<VRB>(vr)) << 4);
+    }
+    auto dma = [&](int j, char *kd, char *vd) __attribute__((always_inline)) {
+        const int kv0 = j * BC;
+        const auto krs = make_rsrc(p.k + base8 + static_cast<long long>(kv0) * rs, (long long)(n - kv0) * rs);
+#pragma unroll
+        for (int i = 0; i < KBLK / NW; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, LDS_PTR(void, kd + (wave + NW * i) * 1024), 16, kvo,
+                                                     NW * i * (1024 / KRB) * rs, 0, 0);
+        // V^T rows are np bytes apart, so a 64-key tile never crosses a row;
+        // keys past n hold the zero padding
+        const auto vrs = make_rsrc(vt + kv0, (long long)D * np - kv0);
+#pragma unroll
+        for (int i = 0; i < VBLK / NW; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, LDS_PTR(void, vd + (wave + NW * i) * 1024), 16, vvo,
+                                                     NW * i * (1024 / VRB) * np, 0, 0);
+    };
+
+    // fragment reads: lane (c, hh) reads 32 bytes = chunks 2 kh', 2 kh' + 1
+    // of a row (kh' = 4 ks + ... for K, hh for V^T)
+    auto row32 = [&](const char *tile, int row, int chunk0, auto rb_) __attribute__((always_inline)) -> i32x8 {
+        constexpr int RB = decltype(rb_)::value;
+        const int s = fp8_swz<RB>(row);
+        const u32x4 lo = *reinterpret_cast<const u32x4 *>(tile + row * RB + ((chunk0 ^ s) << 4));
+        const u32x4 hi = *reinterpret_cast<const u32x4 *>(tile + row * RB + (((chunk0 + 1) ^ s) << 4));
+        return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    };
+    using KRBc = std::integral_constant<int, KRB>;
+    using VRBc = std::integral_constant<int, VRB>;
+
+    const int kv_end = CAUSAL ? min(n, q0 + BR) : n;
+    const int nkv = (kv_end + BC - 1) / BC;
+    const int nkv_w = CAUSAL ? min(nkv, (wrow0 + 31) / BC + 1) : nkv;
+
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    dma(0, k_lds0, v_lds0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    auto tile = [&](const char *ktile, const char *vtile, int j, bool need_mask) __attribute__((always_inline)) {
+        const int kv0 = j * BC;
+        // S^T for the two 32-key blocks: lane (c, hh) register 4 g + r holds
+        // key kv0 + 32 kb + 8 g + 4 hh + r of query wrow0 + c
+        f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    row32(ktile, kb * 32 + c, 4 * ks + 2 * hh, KRBc{}), qf[ks], s[kb], 0, 0, 0, 0, 0, 0);
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int key = kv0 + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+                    const bool off = key >= n || (CAUSAL && key > wrow0 + c);
+                    s[kb][e] = off ? -INFINITY : s[kb][e];
+                }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
+        mx = xhalf_max(mx);
+        const float mt = (mx == -INFINITY) ? -INFINITY : mx * cs;
+        const float m_new = fmaxf(m_run, mt);
+        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        const bool grow = m_new > m_run;
+        m_run = m_new;
+        l_run *= alpha;
+        if (__ballot(grow) != 0) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+        }
+        // P, its row sum, and E4M3 codes of 2^8 P, four keys per register
+        int pk[2][4];
+        float rsum = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float pv[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * g + r], cs, -m_use));
+                    rsum += pv[r];
+                }
+                pk[kb][g] = pack_fp8x4(pv[0] * kFp8PScale, pv[1] * kFp8PScale, pv[2] * kFp8PScale,
+                                       pv[3] * kFp8PScale);
+            }
+        l_run += rsum;
+        // lower half takes block 0's keys, upper half block 1's, in key order
+        i32x8 pb;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(pk[0][g], pk[1][g], false, false);
+            pb[2 * g] = sw[0];
+            pb[2 * g + 1] = sw[1];
+        }
+        // O^T += V^T P^T: A = V^T rows db*32 + c, keys 32 hh .. +32
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+            oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(row32(vtile, db * 32 + c, 2 * hh, VRBc{}), pb,
+                                                                      oacc[db], 0, 0, 0, 0, 0, 0);
+    };
+    for (int j = 0; j < nkv; ++j) {
+        const int par = j & 1;
+        char *kcur = par ? k_lds1 : k_lds0;
+        char *vcur = par ? v_lds1 : v_lds0;
+        if (j + 1 < nkv) dma(j + 1, par ? k_lds0 : k_lds1, par ? v_lds0 : v_lds1);
+        if (j < nkv_w) {
+            const int kv0 = j * BC;
+            const bool need_mask = (CAUSAL && kv0 + BC - 1 > wrow0) || kv0 + BC > n;
+            tile(kcur, vcur, j, need_mask);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    // epilogue: O = O^T dv / (2^8 l), LSE = (m + log2 l) ln 2
+    const float l = xhalf_sum(l_run);
+    const float inv = l > 0.0f ? dv / (kFp8PScale * l) : 0.0f;
+    const long long obase = (static_cast<long long>(b) * n * p.H + h) * D;
+    const auto ors = make_rsrc(p.o + obase + static_cast<long long>(wrow0) * p.H * D,
+                               (long long)(n - wrow0) * p.H * D * 2);
+    const int voff_o = c * p.H * D * 2;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int col = db * 32 + g4 * 8 + hh * 4;
+            const u32x2 v2 = {pack_bf16x2(oacc[db][g4 * 4 + 0] * inv, oacc[db][g4 * 4 + 1] * inv),
+                              pack_bf16x2(oacc[db][g4 * 4 + 2] * inv, oacc[db][g4 * 4 + 3] * inv)};
+            __builtin_amdgcn_raw_buffer_store_b64(v2, ors, voff_o + col * 2, 0, 0);
+        }
+    const int qrow = wrow0 + c;
+    if (qrow < n && hh == 0)
+        p.lse[static_cast<long long>(bh) * n + qrow] = l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// Quantisation: descale[bh] = amax / 448 (1 for an all-zero head), codes =
+// E4M3(x * (1 / descale)), every step in fp32 with IEEE rounding.
+
+__global__ void __launch_bounds__(256) fa_fp8_amax_kernel(QuantParams p) {
+    const int bh = blockIdx.x;
+    const int b = bh / p.H, h = bh - b * p.H;
+    const int chunks = p.d / 8;                        // 16-byte chunks per row
+    const long long total = static_cast<long long>(p.N) * chunks;
+    float m = 0.0f;
+    for (long long t = threadIdx.x; t < total; t += 256) {
+        const long long i = t / chunks;
+        const int cc = static_cast<int>(t - i * chunks);
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(
+            p.x + ((static_cast<long long>(b) * p.N + i) * p.H + h) * p.d + cc * 8);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            m = fmaxf(m, fabsf(__uint_as_float(w[k] << 16)));
+            m = fmaxf(m, fabsf(__uint_as_float(w[k] & 0xffff0000u)));
+        }
+    }
+    __shared__ float red[256];
+    red[threadIdx.x] = m;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if (threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) p.descale[bh] = red[0] > 0.0f ? red[0] / 448.0f : 1.0f;
+}
+
+// one thread per (token, 4 columns); transposed: 64 consecutive tokens of a
+// column are written by the 64 lanes of a wave (one 64-byte row segment),
+// rows padded with zero codes to np = ceil(N/64)*64 tokens
+__global__ void __launch_bounds__(256) fa_fp8_quant_kernel(QuantParams p) {
+    const long long t = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+    const int q4 = p.d / 4;
+    const int np = (p.N + 63) / 64 * 64;
+    long long i, bh;
+    int cq;
+    if (p.transpose) {
+        // t = ((bh * q4 + cq) * np + i): lanes run along tokens
+        const long long per = static_cast<long long>(np);
+        i = t % per;
+        const long long r = t / per;
+        cq = static_cast<int>(r % q4);
+        bh = r / q4;
+    } else {
+        // t = ((b * N + i) * H + h) * q4 + cq: lanes run along columns
+        cq = static_cast<int>(t % q4);
+        const long long r = t / q4;
+        const int h = static_cast<int>(r % p.H);
+        const long long bi = r / p.H;
+        i = bi % p.N;
+        bh = (bi / p.N) * p.H + h;
+    }
+    if (bh >= static_cast<long long>(p.B) * p.H) return;
+    const int b = static_cast<int>(bh / p.H), h = static_cast<int>(bh % p.H);
+    if (i >= p.N) {  // transposed padding
+        uint8_t *row = p.x8 + (bh * p.d + cq * 4) * np + i;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) row[static_cast<long long>(k) * np] = 0;
+        return;
+    }
+    const float inv = 1.0f / p.descale[bh];
+    const u32x2 w = *reinterpret_cast<const u32x2 *>(
+        p.x + ((static_cast<long long>(b) * p.N + i) * p.H + h) * p.d + cq * 4);
+    const float x0 = __uint_as_float(w[0] << 16) * inv, x1 = __uint_as_float(w[0] & 0xffff0000u) * inv;
+    const float x2 = __uint_as_float(w[1] << 16) * inv, x3 = __uint_as_float(w[1] & 0xffff0000u) * inv;
+    const int codes = pack_fp8x4(x0, x1, x2, x3);
+    if (p.transpose) {
+        uint8_t *row = p.x8 + (bh * p.d + cq * 4) * np + i;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) row[static_cast<long long>(k) * np] = static_cast<uint8_t>(codes >> (8 * k));
+    } else {
+        *reinterpret_cast<int *>(p.x8 + ((static_cast<long long>(b) * p.N + i) * p.H + h) * p.d + cq * 4) = codes;
+    }
+}
+
+template <int D>
+KernelFp8Fn select_fp8(bool causal) {
+    return causal ? fa_fp8_fwd_kernel<D, true> : fa_fp8_fwd_kernel<D, false>;
+}
+
+}  // namespace fa_detail

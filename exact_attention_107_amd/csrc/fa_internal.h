@@ -105,4 +105,27 @@ struct BwdKernels {
 BwdKernels select_bwd_d64(bool causal);
 BwdKernels select_bwd_d128(bool causal);
 
+// FP8 (E4M3) forward and quantisation (fa_fp8_kernel.hpp).
+struct Fp8Params {
+    const uint8_t *q, *k;   // E4M3 codes [B, N, H, d]
+    const uint8_t *vt;      // E4M3 codes of V transposed, [B, H, d, Np],
+                            // Np = ceil(N / 64) * 64, zero padded
+    const float *dq, *dk, *dv;  // per-(b, h) descales [B * H]
+    uint16_t *o;            // bf16 [B, N, H, d]
+    float *lse;             // [B, H, N]
+    int B, H, N;
+    float cs;               // scale * log2(e)
+};
+using KernelFp8Fn = void (*)(Fp8Params);
+constexpr int kFp8Rows = 128;  // query rows per FP8 workgroup (4 waves x 32)
+KernelFp8Fn select_fp8_d64(bool causal);
+KernelFp8Fn select_fp8_d128(bool causal);
+struct QuantParams {
+    const uint16_t *x;      // bf16 [B, N, H, d]
+    uint8_t *x8;            // E4M3 codes [B, N, H, d] or [B, H, d, Np]
+    float *descale;         // [B * H]
+    int B, H, N, d, transpose;
+};
+int launch_quant(const QuantParams &qp, void *stream);
+
 }  // namespace fa_detail

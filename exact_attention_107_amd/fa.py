@@ -21,7 +21,7 @@ EXP_HW, EXP_POLY, EXP_MIXED = 0, 1, 2
 RESCALE_ALWAYS, RESCALE_STRICT, RESCALE_THRESHOLD = 0, 1, 2
 EXPORTS = ("fa_fwd", "fa_fwd_variant", "fa_strerror", "fa_tile_rows", "fa_tile_keys",
            "fa_fwd_splitkv", "fa_merge", "fa_split_range", "fa_num_splits", "fa_bwd",
-           "fa_bwd_workspace_floats")
+           "fa_bwd_workspace_floats", "fa_fwd_fp8", "fa_quantize_fp8", "fa_fp8_vt_stride")
 
 _lib = None
 
@@ -66,6 +66,12 @@ def load(path: str | None = None):
     lib.fa_bwd.restype = i32
     lib.fa_bwd_workspace_floats.argtypes = [i32, i32, i32]
     lib.fa_bwd_workspace_floats.restype = ctypes.c_longlong
+    lib.fa_fwd_fp8.argtypes = [vp] * 8 + [i32, i32, i32, i32, ctypes.c_float, i32, vp]
+    lib.fa_fwd_fp8.restype = i32
+    lib.fa_quantize_fp8.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    lib.fa_quantize_fp8.restype = i32
+    lib.fa_fp8_vt_stride.argtypes = [i32]
+    lib.fa_fp8_vt_stride.restype = i32
     if path is None:
         _lib = lib
     return lib
@@ -309,3 +315,69 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse:
     if rc != 0:
         raise FaError(rc, strerror(rc))
     return dq, dk, dv
+
+
+def fp8_vt_stride(N: int) -> int:
+    return int(load().fa_fp8_vt_stride(int(N)))
+
+
+def quantize_fp8(x: torch.Tensor, *, transpose: bool = False, out: torch.Tensor | None = None,
+                 descale: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None):
+    """Per-(b, h) E4M3 quantisation of bf16 ``x [B, N, H, d]`` (``fa_quantize_fp8``).
+
+    Returns ``(codes, descale)``: uint8 codes ``[B, N, H, d]`` (or ``[B, H, d,
+    Np]`` when ``transpose``) and fp32 ``descale [B, H]``.
+    """
+    lib = load()
+    dev = x.device
+    _check(x, "x", torch.bfloat16, dev)
+    B, N, H, d = _dense_shape(x)
+    shape = (B, H, d, fp8_vt_stride(N)) if transpose else (B, N, H, d)
+    out = torch.empty(shape, dtype=torch.uint8, device=dev) if out is None else out
+    descale = torch.empty((B, H), dtype=torch.float32, device=dev) if descale is None else descale
+    _check(out, "out", torch.uint8, dev)
+    _check(descale, "descale", torch.float32, dev)
+    if tuple(out.shape) != shape or tuple(descale.shape) != (B, H):
+        raise ValueError(f"out must be {shape} and descale {(B, H)}")
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = lib.fa_quantize_fp8(x.data_ptr(), out.data_ptr(), descale.data_ptr(), B, H, N, d,
+                                 int(bool(transpose)), ctypes.c_void_p(s.cuda_stream))
+    if rc != 0:
+        raise FaError(rc, strerror(rc))
+    return out, descale
+
+
+def fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, vt8: torch.Tensor, descale_q: torch.Tensor,
+            descale_k: torch.Tensor, descale_v: torch.Tensor, *, causal: bool = False,
+            scale: float | None = None, out: torch.Tensor | None = None,
+            lse: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None):
+    """FP8 forward (``fa_fwd_fp8``): E4M3 ``q8, k8 [B, N, H, d]``, ``vt8
+    [B, H, d, Np]``, fp32 descales ``[B, H]``.  Returns bf16 ``o`` and fp32
+    ``lse``."""
+    lib = load()
+    dev = q8.device
+    for t, name in ((q8, "q8"), (k8, "k8"), (vt8, "vt8")):
+        _check(t, name, torch.uint8, dev)
+    B, N, H, d = _dense_shape(q8)
+    if tuple(k8.shape) != (B, N, H, d) or tuple(vt8.shape) != (B, H, d, fp8_vt_stride(N)):
+        raise ValueError("k8 must be like q8 and vt8 [B, H, d, fp8_vt_stride(N)]")
+    for t, name in ((descale_q, "descale_q"), (descale_k, "descale_k"), (descale_v, "descale_v")):
+        _check(t, name, torch.float32, dev)
+        if tuple(t.shape) != (B, H):
+            raise ValueError(f"{name} must be {(B, H)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty((B, N, H, d), dtype=torch.bfloat16, device=dev) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if lse is None else lse
+    _check(out, "out", torch.bfloat16, dev)
+    _check(lse, "lse", torch.float32, dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = lib.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), descale_q.data_ptr(),
+                            descale_k.data_ptr(), descale_v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                            B, H, N, d, ctypes.c_float(scale), int(bool(causal)),
+                            ctypes.c_void_p(s.cuda_stream))
+    if rc != 0:
+        raise FaError(rc, strerror(rc))
+    return out, lse

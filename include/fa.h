@@ -223,6 +223,43 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o,
  * invalid shape). */
 long long fa_bwd_workspace_floats(int B, int H, int N);
 
+/*
+ * FP8 forward (dense layout, d = 64 or 128).  The FlashAttention-3 notes of
+ * "FlashAttention 1-4 explained" run the forward's products on FP8 matrix
+ * units; here Q K^T and P V both run on E4M3 operands (OCP E4M3: bias 7,
+ * largest finite 448, 0x7f/0xff NaN) with fp32 accumulation.  Scaling is per
+ * (b, h): a tensor's real values are code * descale[b * H + h].
+ *   q8, k8     device E4M3 codes [B, N, H, d].
+ *   vt8        device E4M3 codes of V transposed, [B, H, d, Np] with
+ *              Np = fa_fp8_vt_stride(N) = ceil(N / 64) * 64; the padding
+ *              columns must hold finite codes (fa_quantize_fp8 writes 0).
+ *   descale_q, descale_k, descale_v   device fp32 [B * H].
+ *   o, lse     device outputs: bf16 [B, N, H, d], fp32 [B, H, N].
+ *   B, H, N, scale, causal, stream    as fa_fwd.
+ * P = exp(s - m) is rounded to E4M3 after scaling by 2^8 (P <= 1: the
+ * running max is exact, strict rescale), so each weight carries a relative
+ * rounding error of at most 2^-4; the row sum and LSE come from the fp32 P.
+ */
+int fa_fwd_fp8(const void *q8, const void *k8, const void *vt8,
+               const float *descale_q, const float *descale_k,
+               const float *descale_v, void *o, float *lse, int B, int H,
+               int N, int d, float scale, int causal, hipStream_t stream);
+
+/*
+ * fa_quantize_fp8: per-(b, h) E4M3 quantisation of a bf16 tensor x
+ * [B, N, H, d] (d = 64, 128 or 256): descale[b * H + h] = amax / 448 over
+ * that head (1 for an all-zero head) and codes = E4M3(x * (1 / descale)),
+ * rounded to nearest even, every step in fp32.  transpose = 0 writes x8 as
+ * [B, N, H, d]; transpose != 0 writes [B, H, d, fa_fp8_vt_stride(N)] with
+ * zero codes in the padding (the V layout of fa_fwd_fp8).  Two kernels on
+ * `stream`; errors as fa_fwd.
+ */
+int fa_quantize_fp8(const void *x, void *x8, float *descale, int B, int H,
+                    int N, int d, int transpose, hipStream_t stream);
+
+/* Row stride (keys) of the transposed FP8 V layout: ceil(N / 64) * 64. */
+int fa_fp8_vt_stride(int N);
+
 /* Static, NUL-terminated description of an fa_status code. */
 const char *fa_strerror(int code);
 

@@ -1,0 +1,169 @@
+"""FP8 (E4M3) forward and quantisation, HIP path vs the oracle, through the C
+ABI (needs an MI355X).
+
+Quantisation is compared bit for bit (codes and descales).  The FP8 forward
+is compared with the exact attention of the dequantised inputs under
+per-element bounds derived from the two lossy steps:
+  * the E4M3 products are accumulated with a relative error of at most
+    2^-11 of the sum of the products' magnitudes (measured on the MFMA:
+    worst 2^-11.9 over 64k random dot products; small products are truncated
+    against the largest), so a score carries d_ij = 2^-11 scale
+    sum_k |q_ik k_jk|;
+  * the weights are rounded to E4M3 (relative 2^-4 for normal codes; below
+    the normal range an absolute 2^-18 of the row max).
+With P_ij the exact normalised weights and v_j the dequantised value rows,
+    |dO_i| <= sum_j P_ij (2^-4 + e^(2 d_ij) - 1) |v_j| + 2^-18 sum_j |v_j|
+              + 2^-8 |O_i| + 1e-5        (bf16 output, fp32 accumulation),
+    |dLSE_i| <= max_j d_ij + 1e-5        (the row sum is taken from fp32 P)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_107_amd import fa
+from exact_attention_107_amd.workloads import RUNS, Run, make_inputs
+from gpu_helpers import from_dev, sample_rows
+from oracle import fp8 as ofp8
+
+pytestmark = pytest.mark.gpu
+
+
+def _codes_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _quantized(inp):
+    q8, dq = ofp8.quantize(inp["q"])
+    k8, dk = ofp8.quantize(inp["k"])
+    vt8, dv = ofp8.quantize(inp["v"], transpose=True)
+    return q8, k8, vt8, dq, dk, dv
+
+
+ACC_REL = 2.0 ** -11   # E4M3 MFMA accumulation, relative to sum |products|
+
+
+def _bound_rows(q8, k8, vt8, dq, dk, dv, scale, causal, rows):
+    """Per-element O bounds and per-row LSE bounds for the (b, h, i) rows."""
+    N = q8.shape[1]
+    Q = ofp8.e4m3_decode(q8) * dq[:, None, :, None]
+    K = ofp8.e4m3_decode(k8) * dk[:, None, :, None]
+    Vt = ofp8.e4m3_decode(vt8[..., :N]) * dv[:, :, None, None]
+    sc = float(np.float32(scale))
+    out = np.zeros((len(rows), q8.shape[3]))
+    lse_b = np.zeros(len(rows))
+    for r, (b, h, i) in enumerate(rows):
+        nvis = i + 1 if causal else N
+        s = (K[b, :nvis, h] @ Q[b, i, h]) * sc
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        delta = ACC_REL * sc * (np.abs(K[b, :nvis, h]) @ np.abs(Q[b, i, h]))
+        av = np.abs(Vt[b, h][:, :nvis])
+        out[r] = av @ (p * (2.0 ** -4 + np.expm1(2 * delta))) + 2.0 ** -18 * av.sum(axis=1)
+        lse_b[r] = delta.max() + 1e-5
+    return out, lse_b
+
+
+def _run_fp8(q8, k8, vt8, dq, dk, dv, scale, causal):
+    o, lse = fa.fwd_fp8(_codes_dev(q8), _codes_dev(k8), _codes_dev(vt8), _codes_dev(dq), _codes_dev(dk),
+                        _codes_dev(dv), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _check_rows(inp, causal, q8, k8, vt8, dq, dk, dv, o, lse, rows, what):
+    o_ref, l_ref = ofp8.attention(q8, k8, vt8, dq, dk, dv, scale=inp["scale"], causal=causal, rows=rows)
+    rt = torch.from_numpy(rows)
+    og = from_dev(o[rt[:, 0].cuda(), rt[:, 2].cuda(), rt[:, 1].cuda()])
+    lg = lse[rt[:, 0].cuda(), rt[:, 1].cuda(), rt[:, 2].cuda()].cpu().numpy().astype(np.float64)
+    bound, lse_bound = _bound_rows(q8, k8, vt8, dq, dk, dv, inp["scale"], causal, rows)
+    bound = bound + 2.0 ** -8 * np.abs(o_ref) + 1e-5
+    err = np.abs(og - o_ref)
+    lerr = np.abs(lg - l_ref)
+    print(f"{what}: max|dO| {err.max():.3e} mean|dO| {err.mean():.3e} max err/bound {np.max(err / bound):.3f} "
+          f"max|dLSE| {lerr.max():.2e} max dLSE/bound {np.max(lerr / lse_bound):.3f}")
+    assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg))
+    assert np.all(err <= bound), f"{what}: error above the E4M3 bound, worst ratio {np.max(err / bound):.3f}"
+    assert np.all(lerr <= lse_bound), f"{what}: LSE above its bound, worst ratio {np.max(lerr / lse_bound):.3f}"
+
+
+def _all_rows(B, H, N):
+    return np.array([(b, h, i) for b in range(B) for h in range(H) for i in range(N)], dtype=np.int64)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("transpose", [False, True])
+def test_quantize_bit_exact(d, transpose):
+    inp = make_inputs(Run("q", 2, 3, 130, d, False, 81, sigma_qk=2.0))
+    x = inp["q"].copy()
+    x[1, :, 2, :] = 0  # an all-zero head
+    codes, ds = fa.quantize_fp8(torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda(),
+                                transpose=transpose)
+    torch.cuda.synchronize()
+    ref_c, ref_d = ofp8.quantize(x, transpose=transpose)
+    assert np.array_equal(ds.cpu().numpy(), ref_d)
+    assert np.array_equal(codes.cpu().numpy(), ref_c)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_fwd_small_ragged(d, causal):
+    inp = make_inputs(Run("f8", 2, 3, 300, d, causal, 82))
+    qz = _quantized(inp)
+    o, lse = _run_fp8(*qz, inp["scale"], causal)
+    _check_rows(inp, causal, *qz, o, lse, _all_rows(2, 3, 300), f"d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("N", [1, 63, 64, 65, 130])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_fwd_edge_lengths(N, causal):
+    inp = make_inputs(Run("f8e", 1, 2, N, 128, causal, 400 + N))
+    qz = _quantized(inp)
+    o, lse = _run_fp8(*qz, inp["scale"], causal)
+    _check_rows(inp, causal, *qz, o, lse, _all_rows(1, 2, N), f"N={N} causal={causal}")
+
+
+def test_fp8_fwd_wide_logits():
+    inp = make_inputs(Run("f8w", 1, 2, 500, 128, False, 83, sigma_qk=3.0, boost_frac=0.01))
+    qz = _quantized(inp)
+    o, lse = _run_fp8(*qz, inp["scale"], False)
+    _check_rows(inp, False, *qz, o, lse, _all_rows(1, 2, 500), "wide logits")
+
+
+def test_fp8_fwd_deterministic():
+    inp = make_inputs(Run("f8d", 1, 2, 700, 128, True, 84))
+    qz = _quantized(inp)
+    a = _run_fp8(*qz, inp["scale"], True)
+    b = _run_fp8(*qz, inp["scale"], True)
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16)) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("name", ["wide", "mid_causal"])
+def test_fp8_fwd_full_size_sampled(name):
+    """The benchmark shapes at full size on sampled rows."""
+    run = RUNS[name]
+    inp = make_inputs(run)
+    qz = _quantized(inp)
+    o, lse = _run_fp8(*qz, inp["scale"], run.causal)
+    rows = sample_rows(inp, 128, seed=9)
+    _check_rows(inp, run.causal, *qz, o, lse, rows, name)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+def test_fp8_end_to_end_against_bf16_oracle():
+    """GPU quantisation + FP8 forward against the exact bf16-input attention:
+    the inputs' own E4M3 rounding adds error, so only its size is checked
+    loosely (informational)."""
+    import oracle
+    inp = make_inputs(Run("f8x", 1, 2, 256, 128, False, 85))
+    x = {n: torch.from_numpy(inp[n].view(np.int16)).view(torch.bfloat16).cuda() for n in ("q", "k", "v")}
+    q8, dq = fa.quantize_fp8(x["q"])
+    k8, dk = fa.quantize_fp8(x["k"])
+    vt8, dv = fa.quantize_fp8(x["v"], transpose=True)
+    o, lse = fa.fwd_fp8(q8, k8, vt8, dq, dk, dv, scale=inp["scale"])
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(inp["q"], inp["k"], inp["v"], scale=inp["scale"], causal=False)
+    err = np.abs(from_dev(o) - o_ref)
+    print(f"end to end: max|dO| {err.max():.3e} mean|dO| {err.mean():.3e} "
+          f"max|dLSE| {np.abs(lse.cpu().numpy() - l_ref).max():.3e}")
+    assert err.mean() <= 2e-2
