@@ -8,10 +8,11 @@
 //    each lane reading 32 consecutive bytes of its key's row; Q (B operand)
 //    held in VGPRs for the whole kernel.  Each lane again owns one query row.
 //  * P = 2^(s c - m) (strict rescale: m is the running row max, so P <= 1) is
-//    scaled by 2^8 and rounded to E4M3 (v_cvt_pk_fp8_f32, nearest even): the
-//    scale keeps values down to 2^-18 of the row max out of the flush-to-zero
-//    range, and 2^8 P <= 256 stays below the E4M3 maximum 448.  The row sum l
-//    is accumulated from the fp32 P.
+//    computed directly as 2^8 P = 2^(s c - (m - 8)) and rounded to E4M3
+//    (v_cvt_pk_fp8_f32, nearest even): the factor keeps values down to 2^-18
+//    of the row max out of the flush-to-zero range, and 2^8 P <= 256 stays
+//    below the E4M3 maximum 448.  The row sum l is accumulated from the fp32
+//    weights.
 //  * O^T += V^T P^T takes P as the B operand, whose 64 keys must sit as 32
 //    consecutive keys per lane half.  The accumulator gives lane half hh the
 //    keys 8g + 4hh + r of both 32-key blocks; one v_permlane32_swap per
@@ -21,7 +22,10 @@
 //    [B, H, d, Np] with rows padded with zero codes to Np = ceil(N/64)*64) so
 //    that its A operand is again 32 consecutive bytes of one LDS row.
 //  * Scores are scaled by scale * descale_q * descale_k (folded into c) and
-//    the output by descale_v / (2^8 l).
+//    the output by descale_v / l.
+//  * Software pipeline as in the bf16 kernel: the S(j+1) MFMAs are issued
+//    before the weights of S(j) are computed, the P V(j) MFMAs before the row
+//    max of S(j+1).
 // LDS rows are 64 or 128 bytes; their 16-byte chunks are XOR-permuted so
 // that the 16 rows of one fragment read cover 16 distinct bank groups.
 
@@ -51,7 +55,8 @@ __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
 }
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kFp8Waves * 64) fa_fp8_fwd_kernel(Fp8Params p) {
+__global__ void __launch_bounds__(kFp8Waves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+fa_fp8_fwd_kernel(Fp8Params p) {
     constexpr int NW = kFp8Waves, BC = kFp8Keys, BR = NW * 32;
     constexpr int KS = D / 64;          // 64-wide k steps of Q K^T
     constexpr int NDB = D / 32;         // 32-wide d blocks of O^T
@@ -118,22 +123,6 @@ __global__ void __launch_bounds__(kFp8Waves * 64) fa_fp8_fwd_kernel(Fp8Params p)
         const int vr = pos / VRB, vpc = (pos % VRB) / 16;
         vvo = vr * np + ((vpc ^ fp8_swz<VRB>(vr)) << 4);
     }
-    auto dma = [&](int j, char *kd, char *vd) __attribute__((always_inline)) {
-        const int kv0 = j * BC;
-        const auto krs = make_rsrc(p.k + base8 + static_cast<long long>(kv0) * rs, (long long)(n - kv0) * rs);
-#pragma unroll
-        for (int i = 0; i < KBLK / NW; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, LDS_PTR(void, kd + (wave + NW * i) * 1024), 16, kvo,
-                                                     NW * i * (1024 / KRB) * rs, 0, 0);
-        // V^T rows are np bytes apart, so a 64-key tile never crosses a row;
-        // keys past n hold the zero padding
-        const auto vrs = make_rsrc(vt + kv0, (long long)D * np - kv0);
-#pragma unroll
-        for (int i = 0; i < VBLK / NW; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, LDS_PTR(void, vd + (wave + NW * i) * 1024), 16, vvo,
-                                                     NW * i * (1024 / VRB) * np, 0, 0);
-    };
-
     // fragment reads: lane (c, hh) reads 32 bytes = chunks 2 kh', 2 kh' + 1
     // of a row (kh' = 4 ks + ... for K, hh for V^T)
     auto row32 = [&](const char *tile, int row, int chunk0, auto rb_) __attribute__((always_inline)) -> i32x8 {
@@ -153,33 +142,38 @@ __global__ void __launch_bounds__(kFp8Waves * 64) fa_fp8_fwd_kernel(Fp8Params p)
     f32x16 oacc[NDB];
 #pragma unroll
     for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.0f;
+    // m_run: running row max (log2 units); the weights are 2^(s c - m + 8) =
+    // 2^8 P, so l_run sums 2^8 P as well
+    float m_run = -INFINITY, l_run = 0.0f, m_use8 = 0.0f, alpha = 1.0f;
+    bool rescale_o = false;
 
-    dma(0, k_lds0, v_lds0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    auto tile = [&](const char *ktile, const char *vtile, int j, bool need_mask) __attribute__((always_inline)) {
-        const int kv0 = j * BC;
-        // S^T for the two 32-key blocks: lane (c, hh) register 4 g + r holds
-        // key kv0 + 32 kb + 8 g + 4 hh + r of query wrow0 + c
-        f32x16 s[2] = {f32x16{}, f32x16{}};
+    // S^T of one 64-key tile: lane (c, hh) register 4 g + r of s[kb] holds
+    // key 32 kb + 8 g + 4 hh + r of query wrow0 + c
+    auto s_mfma = [&](f32x16 (&s)[2], const char *ktile) __attribute__((always_inline)) {
+        s[0] = f32x16{};
+        s[1] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
                 s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                     row32(ktile, kb * 32 + c, 4 * ks + 2 * hh, KRBc{}), qf[ks], s[kb], 0, 0, 0, 0, 0, 0);
-        if (need_mask) {
+    };
+    auto need_mask = [&](int j) { return (CAUSAL && j * BC + BC - 1 > wrow0) || j * BC + BC > n; };
+    auto s_mask = [&](f32x16 (&s)[2], int j) __attribute__((always_inline)) {
+        const int kv0 = j * BC;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int key = kv0 + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
-                    const bool off = key >= n || (CAUSAL && key > wrow0 + c);
-                    s[kb][e] = off ? -INFINITY : s[kb][e];
-                }
-        }
+            for (int e = 0; e < 16; ++e) {
+                const int key = kv0 + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+                const bool off = key >= n || (CAUSAL && key > wrow0 + c);
+                s[kb][e] = off ? -INFINITY : s[kb][e];
+            }
+    };
+    // running max update from the tile's raw row max (strict: the reference
+    // is always the exact running max, so P <= 1)
+    auto s_update = [&](const f32x16 (&s)[2]) __attribute__((always_inline)) {
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -189,17 +183,15 @@ __global__ void __launch_bounds__(kFp8Waves * 64) fa_fp8_fwd_kernel(Fp8Params p)
         const float mt = (mx == -INFINITY) ? -INFINITY : mx * cs;
         const float m_new = fmaxf(m_run, mt);
         const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        const bool grow = m_new > m_run;
+        alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        rescale_o = __ballot(m_new > m_run) != 0;
         m_run = m_new;
+        m_use8 = m_use - 8.0f;
         l_run *= alpha;
-        if (__ballot(grow) != 0) {
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-        }
-        // P, its row sum, and E4M3 codes of 2^8 P, four keys per register
+    };
+    // 2^8 P in E4M3, its sum, the regrouping into operand order, and
+    // O^T += V^T P^T
+    auto p_pv = [&](const f32x16 (&s)[2], const char *vtile) __attribute__((always_inline)) {
         int pk[2][4];
         float rsum = 0.0f;
 #pragma unroll
@@ -209,11 +201,10 @@ __global__ void __launch_bounds__(kFp8Waves * 64) fa_fp8_fwd_kernel(Fp8Params p)
                 float pv[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * g + r], cs, -m_use));
+                    pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * g + r], cs, -m_use8));
                     rsum += pv[r];
                 }
-                pk[kb][g] = pack_fp8x4(pv[0] * kFp8PScale, pv[1] * kFp8PScale, pv[2] * kFp8PScale,
-                                       pv[3] * kFp8PScale);
+                pk[kb][g] = pack_fp8x4(pv[0], pv[1], pv[2], pv[3]);
             }
         l_run += rsum;
         // lower half takes block 0's keys, upper half block 1's, in key order
@@ -224,29 +215,82 @@ __global__ void __launch_bounds__(kFp8Waves * 64) fa_fp8_fwd_kernel(Fp8Params p)
             pb[2 * g] = sw[0];
             pb[2 * g + 1] = sw[1];
         }
-        // O^T += V^T P^T: A = V^T rows db*32 + c, keys 32 hh .. +32
+        if (rescale_o) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+        }
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
             oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(row32(vtile, db * 32 + c, 2 * hh, VRBc{}), pb,
                                                                       oacc[db], 0, 0, 0, 0, 0, 0);
     };
-    for (int j = 0; j < nkv; ++j) {
-        const int par = j & 1;
-        char *kcur = par ? k_lds1 : k_lds0;
-        char *vcur = par ? v_lds1 : v_lds0;
-        if (j + 1 < nkv) dma(j + 1, par ? k_lds0 : k_lds1, par ? v_lds0 : v_lds1);
-        if (j < nkv_w) {
-            const int kv0 = j * BC;
-            const bool need_mask = (CAUSAL && kv0 + BC - 1 > wrow0) || kv0 + BC > n;
-            tile(kcur, vcur, j, need_mask);
+
+    // Pipeline: LDS holds K(j+1) and V(j) while K(j+2) and V(j+1) stream in
+    // (into the buffers of K(j) and V(j-1), both consumed before the previous
+    // barrier).  Iteration j issues the S(j+1) MFMAs, then the weights of
+    // S(j) (VALU, independent of them) and the P V(j) MFMAs, then the row max
+    // of S(j+1).
+    f32x16 sa[2], sb[2];
+    auto dma_k = [&](int j, char *kd) __attribute__((always_inline)) {
+        const int kv0 = j * BC;
+        const auto krs = make_rsrc(p.k + base8 + static_cast<long long>(kv0) * rs, (long long)(n - kv0) * rs);
+#pragma unroll
+        for (int i = 0; i < KBLK / NW; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, LDS_PTR(void, kd + (wave + NW * i) * 1024), 16, kvo,
+                                                     NW * i * (1024 / KRB) * rs, 0, 0);
+    };
+    auto dma_v = [&](int j, char *vd) __attribute__((always_inline)) {
+        const int kv0 = j * BC;
+        // V^T rows are np bytes apart, so a 64-key tile never crosses a row;
+        // keys past n hold the zero padding
+        const auto vrs = make_rsrc(vt + kv0, (long long)D * np - kv0);
+#pragma unroll
+        for (int i = 0; i < VBLK / NW; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, LDS_PTR(void, vd + (wave + NW * i) * 1024), 16, vvo,
+                                                     NW * i * (1024 / VRB) * np, 0, 0);
+    };
+    dma_k(0, k_lds0);
+    dma_v(0, v_lds0);
+    if (nkv > 1) dma_k(1, k_lds1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (nkv_w > 0) {
+        s_mfma(sa, k_lds0);
+        if (need_mask(0)) s_mask(sa, 0);
+        s_update(sa);
+    }
+    __syncthreads();  // K(0)'s buffer takes K(2) next
+
+    auto step = [&](auto par_, f32x16 (&cur)[2], f32x16 (&nxt)[2], int j) __attribute__((always_inline)) {
+        constexpr int PAR = decltype(par_)::value;  // j & 1
+        char *kbuf_j = PAR ? k_lds1 : k_lds0;       // held K(j), takes K(j+2)
+        char *kbuf_n = PAR ? k_lds0 : k_lds1;       // holds K(j+1)
+        char *vbuf_j = PAR ? v_lds1 : v_lds0;       // holds V(j)
+        char *vbuf_n = PAR ? v_lds0 : v_lds1;       // held V(j-1), takes V(j+1)
+        if (j + 2 < nkv) dma_k(j + 2, kbuf_j);
+        if (j + 1 < nkv) dma_v(j + 1, vbuf_n);
+        const bool has_next = j + 1 < nkv_w;
+        if (has_next) s_mfma(nxt, kbuf_n);
+        if (j < nkv_w) p_pv(cur, vbuf_j);
+        if (has_next) {
+            if (need_mask(j + 1)) s_mask(nxt, j + 1);
+            s_update(nxt);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+    };
+    int j = 0;
+    for (; j + 1 < nkv; j += 2) {
+        step(std::integral_constant<int, 0>{}, sa, sb, j);
+        step(std::integral_constant<int, 1>{}, sb, sa, j + 1);
     }
+    if (j < nkv) step(std::integral_constant<int, 0>{}, sa, sb, j);
 
-    // epilogue: O = O^T dv / (2^8 l), LSE = (m + log2 l) ln 2
+    // epilogue: O = O^T dv / l (l sums 2^8 P like O), LSE = (m + log2 l - 8) ln 2
     const float l = xhalf_sum(l_run);
-    const float inv = l > 0.0f ? dv / (kFp8PScale * l) : 0.0f;
+    const float inv = l > 0.0f ? dv / l : 0.0f;
     const long long obase = (static_cast<long long>(b) * n * p.H + h) * D;
     const auto ors = make_rsrc(p.o + obase + static_cast<long long>(wrow0) * p.H * D,
                                (long long)(n - wrow0) * p.H * D * 2);
@@ -262,7 +306,7 @@ __global__ void __launch_bounds__(kFp8Waves * 64) fa_fp8_fwd_kernel(Fp8Params p)
         }
     const int qrow = wrow0 + c;
     if (qrow < n && hh == 0)
-        p.lse[static_cast<long long>(bh) * n + qrow] = l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+        p.lse[static_cast<long long>(bh) * n + qrow] = l > 0.0f ? (m_run + log2f(l) - 8.0f) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
