@@ -379,12 +379,13 @@ int fa_fwd_fp8(const void *q8, const void *k8, const void *vt8, const float *des
     fp.H = H;
     fp.N = N;
     fp.cs = scale * kLog2e;
-    const long long n_qt = (static_cast<long long>(N) + kFp8Rows - 1) / kFp8Rows;
+    const int rows_per_tile = fp8_rows_for(d);
+    const long long n_qt = (static_cast<long long>(N) + rows_per_tile - 1) / rows_per_tile;
     const long long grid = static_cast<long long>(B) * H * n_qt;
     if (grid <= 0 || grid > 0x7fffffffLL) return FA_ERR_SHAPE;
     const KernelFp8Fn fn = d == 64 ? select_fp8_d64(causal != 0) : select_fp8_d128(causal != 0);
     (void)hipGetLastError();
-    hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(grid)), dim3(kFp8Rows * 2), 0, stream, fp);
+    hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(grid)), dim3(rows_per_tile * 2), 0, stream, fp);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -37,7 +37,6 @@ namespace fa_detail {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kFp8Waves = kFp8Rows / 32;
 constexpr int kFp8Keys = 64;            // keys per K / V^T tile
 constexpr float kFp8PScale = 256.0f;    // P is stored as E4M3(2^8 P)
 
@@ -55,9 +54,9 @@ __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
 }
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kFp8Waves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(Fp8Geometry<D>::kWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 fa_fp8_fwd_kernel(Fp8Params p) {
-    constexpr int NW = kFp8Waves, BC = kFp8Keys, BR = NW * 32;
+    constexpr int NW = Fp8Geometry<D>::kWaves, BC = kFp8Keys, BR = NW * 32;
     constexpr int KS = D / 64;          // 64-wide k steps of Q K^T
     constexpr int NDB = D / 32;         // 32-wide d blocks of O^T
     constexpr int KRB = D;              // bytes per K row

@@ -117,7 +117,14 @@ struct Fp8Params {
     float cs;               // scale * log2(e)
 };
 using KernelFp8Fn = void (*)(Fp8Params);
-constexpr int kFp8Rows = 128;  // query rows per FP8 workgroup (4 waves x 32)
+// query rows per FP8 workgroup (32 per wave).  Four waves: an FP8 tile is
+// half the bytes of a bf16 one, and eight-wave workgroups measured 5-8 %
+// slower here (one barrier couples twice the waves).
+template <int D> struct Fp8Geometry {
+    static constexpr int kWaves = 4;
+    static constexpr int kRows = kWaves * 32;
+};
+inline int fp8_rows_for(int d) { return d == 128 ? Fp8Geometry<128>::kRows : Fp8Geometry<64>::kRows; }
 KernelFp8Fn select_fp8_d64(bool causal);
 KernelFp8Fn select_fp8_d128(bool causal);
 struct QuantParams {
