@@ -1,0 +1,113 @@
+"""The window-mask / linear-bias oracle against independent routes: the C
+oracle (full, causal, and key ranges), closed forms of the bias, and the
+single-key window; planted mistakes in a copy of it must fail."""
+import os
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.mods as omods
+from exact_attention_107_amd.workloads import Run, make_inputs
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "mods.py")
+
+
+def _inp(N=23, B=2, H=2, d=16, seed=41, sigma=1.0):
+    return make_inputs(Run("m", B, H, N, d, False, seed, sigma_qk=sigma))
+
+
+def pin_unbounded_and_causal(attn, lib):
+    inp = _inp()
+    for left, right, causal in ((-1, -1, False), (-1, 0, True)):
+        o, l = attn(inp["q"], inp["k"], inp["v"], scale=0.3, left=left, right=right)
+        ro, rl = oracle.attention(inp["q"], inp["k"], inp["v"], scale=0.3, causal=causal, lib=lib)
+        assert np.max(np.abs(o - ro)) <= 1e-12 and np.max(np.abs(l - rl)) <= 1e-12, (left, right)
+
+
+def pin_windows_equal_key_ranges(attn, lib):
+    """A window is, per row, the C oracle's attention over a key range."""
+    inp = _inp()
+    B, N, H = 2, 23, 2
+    for left, right in ((3, 0), (0, 2), (4, 5), (-1, 3), (6, -1), (0, 0)):
+        o, l = attn(inp["q"], inp["k"], inp["v"], scale=0.3, left=left, right=right)
+        for i in range(N):
+            lo = 0 if left < 0 else max(0, i - left)
+            hi = N if right < 0 else min(N, i + right + 1)
+            rows = np.array([(b, h, i) for b in range(B) for h in range(H)], dtype=np.int64)
+            ro, rl = oracle.attention(inp["q"], inp["k"], inp["v"], scale=0.3, causal=False, rows=rows,
+                                      key_range=(lo, hi), lib=lib)
+            assert np.max(np.abs(o[rows[:, 0], i, rows[:, 1]] - ro)) <= 1e-12, (left, right, i)
+            assert np.max(np.abs(l[rows[:, 0], rows[:, 1], i] - rl)) <= 1e-12, (left, right, i)
+
+
+def pin_bias_closed_form(attn, lib):
+    """Q = 0: the scores are slope (j - i) alone; causal weights of row i are
+    e^{-slope t} for t = i - j, whose sum is a geometric series."""
+    inp = _inp(N=17, B=1, H=2)
+    q = np.zeros_like(inp["q"])
+    slopes = np.array([0.5, 0.125], np.float32)
+    o, l = attn(q, inp["k"], inp["v"], scale=0.3, left=-1, right=0, slopes=slopes)
+    v = (inp["v"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for h, s in enumerate(slopes.astype(np.float64)):
+        for i in range(17):
+            t = np.arange(i + 1)
+            w = np.exp(-s * t)
+            assert abs(l[0, h, i] - np.log((1 - np.exp(-s * (i + 1))) / (1 - np.exp(-s)))) <= 1e-12
+            ref = (w / w.sum()) @ v[0, i - t, h]
+            assert np.max(np.abs(o[0, i, h] - ref)) <= 1e-12
+
+
+def pin_bias_row_constant_drops_out(attn, lib):
+    """Non-causal: slope (j - i) = slope j - slope i, and the row constant
+    -slope i cancels in the softmax and shifts LSE by it exactly."""
+    inp = _inp(N=19, B=1, H=1)
+    s = np.float32(0.25)
+    o, l = attn(inp["q"], inp["k"], inp["v"], scale=0.3, slopes=np.array([s]))
+    o2, l2 = attn(inp["q"], inp["k"], inp["v"], scale=0.3, slopes=np.array([s]), rows=np.array([[0, 0, 0]]))
+    # row i versus row 0 shifted: O from the same weights over keys (query differs), so check
+    # LSE_i + slope i = ln sum_j exp(scale q_i.k_j + slope j) computed directly
+    Q = (inp["q"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    K = (inp["k"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for i in range(19):
+        z = float(np.float32(0.3)) * (K[0, :, 0] @ Q[0, i, 0]) + float(s) * np.arange(19)
+        ref = np.log(np.sum(np.exp(z - z.max()))) + z.max()
+        assert abs(l[0, 0, i] + float(s) * i - ref) <= 1e-11
+    assert abs(l2[0] - l[0, 0, 0]) <= 1e-15
+
+
+ALL = [pin_unbounded_and_causal, pin_windows_equal_key_ranges, pin_bias_closed_form,
+       pin_bias_row_constant_drops_out]
+
+
+@pytest.mark.parametrize("pin", ALL, ids=lambda p: p.__name__)
+def test_mods_pin(pin, oracle_lib):
+    pin(omods.attention, oracle_lib)
+
+
+MUTANTS = {
+    "left_bound_exclusive": ("ok = ok & (j >= i - left)", "ok = ok & (j > i - left)"),
+    "right_bound_exclusive": ("ok = ok & (j <= i + right)", "ok = ok & (j < i + right)"),
+    "bias_sign": ("+ sl[h] * (keys - i)", "- sl[h] * (keys - i)"),
+    "bias_unscaled_distance": ("+ sl[h] * (keys - i)", "+ sl[h] * keys"),
+    "bias_times_scale": ("+ sl[h] * (keys - i)", "+ sc * sl[h] * (keys - i)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mods_mutant_is_caught(name, oracle_lib):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1
+    mod = types.ModuleType(f"mods_{name}")
+    mod.__dict__["_widen"] = oracle._widen
+    exec(compile(src.replace(old, new).replace("from . import _widen", ""), name, "exec"), mod.__dict__)
+    caught = []
+    for pin in ALL:
+        try:
+            with np.errstate(all="ignore"):
+                pin(mod.attention, oracle_lib)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"
