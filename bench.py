@@ -229,6 +229,39 @@ def fp8_runs(torch, fa):
     return res
 
 
+def masked_runs(torch, fa):
+    """fa_fwd_masked: a causal sliding window of 1024 keys with ALiBi slopes
+    on B=1 H=16 N=16384 d=128 (credited flops: 4 d per visible (query, key)
+    pair), and the plain causal mask through the masked path next to fa_fwd."""
+    from exact_attention_107_amd.workloads import Run, flops, make_inputs
+    r = Run("masked", 1, 16, 16384, 128, False, 1009)
+    log("[bench] masked runs")
+    ri = make_inputs(r)
+    q, k, v = (to_dev(ri[x], torch) for x in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty((r.B, r.H, r.N), dtype=torch.float32, device="cuda")
+    slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / r.H) for h in range(r.H)], dtype=torch.float32,
+                          device="cuda")
+    W = 1024
+    pairs = sum(min(i + 1, W + 1) for i in range(r.N))
+    f_window = 4.0 * r.d * r.H * r.B * pairs
+    f_causal = flops(ri["lengths"], r.H, r.d, True)
+    res = {"shape": f"B={r.B} H={r.H} N={r.N} d={r.d}"}
+    for name, kw, f in (("window1024_alibi", dict(window_left=W, window_right=0, alibi_slopes=slopes), f_window),
+                        ("causal_masked_path", dict(window_left=-1, window_right=0), f_causal)):
+        def launch():
+            fa.fwd_masked(q, k, v, scale=ri["scale"], out=o, lse=lse, **kw)
+        _, ms, _, _ = time_launches(launch, 20, 20, torch)
+        res[name] = {"ms": round(ms, 4), "tflops": round(f / ms / 1e9, 1)}
+
+    def causal():
+        fa.fwd(q, k, v, causal=True, scale=ri["scale"], out=o, lse=lse)
+    _, ms, _, _ = time_launches(causal, 20, 20, torch)
+    res["causal_fa_fwd"] = {"ms": round(ms, 4), "tflops": round(f_causal / ms / 1e9, 1)}
+    del q, k, v, o, lse
+    return res
+
+
 def traffic_for(fingerprint: str):
     try:
         with open(TRAFFIC_FILE) as f:
@@ -369,6 +402,7 @@ def main() -> int:
         out["backward"] = {name: backward_run(torch, fa, name)[0]
                            for name in ("mid", "mid_causal", "bwd_long", "bwd_long_causal")}
         out["fp8"] = fp8_runs(torch, fa)
+        out["masked"] = masked_runs(torch, fa)
 
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")

@@ -314,6 +314,51 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const flo
     return FA_OK;
 }
 
+int fa_fwd_masked(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N, int d,
+                  float scale, int window_left, int window_right, const float *alibi_slopes, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULLPTR;
+    if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128 && d != 256) return FA_ERR_HEAD_DIM;
+    if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_SCALE;
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) || misaligned(lse, 4) ||
+        misaligned(alibi_slopes, 4))
+        return FA_ERR_ALIGN;
+    const long long rows = static_cast<long long>(B) * N * H;
+    const long long elems = rows * d;
+    if (elems <= 0 || elems > (1LL << 46) || !token_stride_ok(H, d)) return FA_ERR_SHAPE;
+    const size_t tb = static_cast<size_t>(elems) * 2, lb = static_cast<size_t>(rows) * 4;
+    const size_t sb = static_cast<size_t>(H) * 4;
+    const void *ins[] = {q, k, v};
+    for (const void *in : ins)
+        if (overlap(o, tb, in, tb) || overlap(lse, lb, in, tb)) return FA_ERR_ALIAS;
+    if (overlap(o, tb, lse, lb)) return FA_ERR_ALIAS;
+    if (alibi_slopes && (overlap(o, tb, alibi_slopes, sb) || overlap(lse, lb, alibi_slopes, sb))) return FA_ERR_ALIAS;
+
+    Params prm{};
+    prm.q = static_cast<const uint16_t *>(q);
+    prm.k = static_cast<const uint16_t *>(k);
+    prm.v = static_cast<const uint16_t *>(v);
+    prm.o = static_cast<uint16_t *>(o);
+    prm.lse = lse;
+    prm.B = B;
+    prm.H = H;
+    prm.N = N;
+    prm.cs = scale * kLog2e;
+    prm.wl = window_left < 0 ? -1 : window_left;
+    prm.wr = window_right < 0 ? -1 : window_right;
+    prm.alibi = alibi_slopes;
+    prm.inv_scale = 1.0f / scale;
+    const int rows_per_tile = tile_rows_for(d);
+    const long long n_qt = (static_cast<long long>(N) + rows_per_tile - 1) / rows_per_tile;
+    prm.n_qt = static_cast<int>(n_qt);
+    const long long grid = static_cast<long long>(B) * H * n_qt;
+    if (grid <= 0 || grid > 0x7fffffffLL) return FA_ERR_SHAPE;
+    const KernelFn fn = d == 64 ? select_mods_d64() : (d == 128 ? select_mods_d128() : select_mods_d256());
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(grid)), dim3(waves_for(d) * 64), 0, stream, prm);
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int fa_fp8_vt_stride(int N) { return N < 1 ? 0 : (N + 63) / 64 * 64; }
 
 int fa_quantize_fp8(const void *x, void *x8, float *descale, int B, int H, int N, int d, int transpose,

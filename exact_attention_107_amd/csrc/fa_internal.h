@@ -19,6 +19,10 @@ struct Params {
     float *op;          // partial outputs, [nsplit][B*N][H][d] fp32
     float *lp;          // partial LSEs, [nsplit][B][H][N] fp32
     int nsplit;         // number of key ranges per query tile
+    // window mask and linear bias (masked instances only)
+    int wl, wr;          // key j visible to query i iff i - wl <= j <= i + wr (< 0: unbounded)
+    const float *alibi;  // per-head slopes [H], or nullptr
+    float inv_scale;     // 1 / scale
 };
 
 using KernelFn = void (*)(Params);
@@ -69,6 +73,10 @@ inline int waves_for(int d) {
 KernelFn select_d64(bool causal, bool varlen, int exp_mode, int rescale_mode);
 KernelFn select_d128(bool causal, bool varlen, int exp_mode, int rescale_mode);
 KernelFn select_d256(bool causal, bool varlen, int exp_mode, int rescale_mode);
+// Window-mask / linear-bias instance (dense layout).
+KernelFn select_mods_d64();
+KernelFn select_mods_d128();
+KernelFn select_mods_d256();
 // Split-KV instance (dense layout, partial results into Params::op / lp).
 KernelFn select_split_d64(bool causal);
 KernelFn select_split_d128(bool causal);

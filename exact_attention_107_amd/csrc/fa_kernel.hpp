@@ -196,7 +196,7 @@ struct Work {
     int split;        // key range (split-KV instances)
 };
 
-template <bool CAUSAL, bool VARLEN, int BR, bool SPLIT>
+template <bool CAUSAL, bool VARLEN, int BR, bool SPLIT, bool MODS = false>
 __device__ __forceinline__ bool decode_work(const Params &p, Work &w) {
     const int wg = blockIdx.x;
     w.split = 0;
@@ -234,7 +234,9 @@ __device__ __forceinline__ bool decode_work(const Params &p, Work &w) {
     } else if constexpr (!VARLEN) {
         const int BH = p.B * p.H;
         int bh, qt;
-        if constexpr (CAUSAL) {
+        // a window with a right edge makes the work grow with the query tile
+        // like the causal mask does
+        if (CAUSAL || (MODS && p.wr >= 0)) {
             // longest tiles (highest query tile) first; wg % 8 picks the XCD,
             // so with BH % 8 == 0 all tiles of one head stay on one XCD
             qt = p.n_qt - 1 - wg / BH;
@@ -324,7 +326,8 @@ __device__ __forceinline__ bool decode_work(const Params &p, Work &w) {
 // consumed before the previous barrier); the barrier that ends the iteration
 // makes them visible.
 
-template <int D, int BC, int NW, int QB, bool CAUSAL, bool VARLEN, int EXPM, int RSM, bool SPLIT = false>
+template <int D, int BC, int NW, int QB, bool CAUSAL, bool VARLEN, int EXPM, int RSM, bool SPLIT = false,
+          bool MODS = false>
 __global__ void __launch_bounds__(NW * 64)
 fa_fwd_kernel(Params p) {
     using SW = Swz<D>;
@@ -348,7 +351,7 @@ fa_fwd_kernel(Params p) {
     __shared__ __attribute__((aligned(1024))) char k_lds0[TB], k_lds1[TB], v_lds0[TB], v_lds1[TB];
 
     Work w;
-    if (!decode_work<CAUSAL, VARLEN, BR, SPLIT>(p, w)) return;
+    if (!decode_work<CAUSAL, VARLEN, BR, SPLIT, MODS>(p, w)) return;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -378,18 +381,25 @@ fa_fwd_kernel(Params p) {
                     bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, voff + kk * 32, 32 * b * static_cast<int>(rs) * 2, 0));
     }
 
-    const int kv_end = CAUSAL ? min(n, q0 + BR) : n;
+    // keys past kv_end are invisible to every row of the workgroup: the causal
+    // diagonal, or the right edge of a window
+    const int kv_end = MODS ? (p.wr < 0 ? n : min(n, q0 + BR + p.wr)) : (CAUSAL ? min(n, q0 + BR) : n);
     // Tiles are numbered from kt0, the first tile of this workgroup's key
-    // range (0 unless the key sequence is split); tile j covers keys
-    // (kt0 + j) * BC ...
+    // range (0 unless the key sequence is split or a window's left edge
+    // hides the first tiles); tile j covers keys (kt0 + j) * BC ...
     // The split divides the tiles this query tile sees (all of the sequence,
     // or up to the diagonal when causal) into nsplit near-equal ranges.
     const int tiles_seen = (kv_end + BC - 1) / BC;
-    const int kt0 = SPLIT ? w.split * tiles_seen / p.nsplit : 0;
+    const int kt0 = SPLIT ? w.split * tiles_seen / p.nsplit
+                          : (MODS && p.wl >= 0 ? max(0, q0 - p.wl) / BC : 0);
     const int kt_end = SPLIT ? (w.split + 1) * tiles_seen / p.nsplit : tiles_seen;
     const int nkv = max(kt_end - kt0, 0);
-    // tiles this wave computes: the causal diagonal ends its work earlier
-    const int nkv_w = CAUSAL ? max(min(kt_end, (wrow0 + RW - 1) / BC + 1) - kt0, 0) : nkv;
+    // tiles this wave computes: the causal diagonal (or the window's right
+    // edge) ends its work earlier
+    int w_end = kt_end;
+    if (CAUSAL) w_end = min(kt_end, (wrow0 + RW - 1) / BC + 1);
+    if (MODS && p.wr >= 0) w_end = min(kt_end, (wrow0 + RW - 1 + p.wr) / BC + 1);
+    const int nkv_w = max(w_end - kt0, 0);
 
     // ---- direct global -> LDS loads ---------------------------------------------
     // K: the tile is 8*D/64 loads of 1 KB (8 rows of one 128-byte plane each);
@@ -489,8 +499,12 @@ fa_fwd_kernel(Params p) {
     // -inf for tail keys (>= n) and, when causal, keys after the query.
     auto need_mask = [&](int j) {
         const int kv0 = (kt0 + j) * BC;
+        if constexpr (MODS)
+            return p.alibi != nullptr || (p.wl >= 0 && kv0 < wrow0 + RW - 1 - p.wl) ||
+                   (p.wr >= 0 && kv0 + BC - 1 > wrow0 + p.wr) || kv0 + BC > n;
         return (CAUSAL && kv0 + BC - 1 > wrow0) || kv0 + BC > n;
     };
+    const float bias_coef = MODS && p.alibi ? p.alibi[w.h] * p.inv_scale : 0.0f;
     auto s_mask = [&](f32x16 (&s)[QB][NKB], int j) {
         const int kv0 = (kt0 + j) * BC;
 #pragma unroll
@@ -501,7 +515,12 @@ fa_fwd_kernel(Params p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = kv0 + kb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-                    const bool off = key >= n || (CAUSAL && key > qrow);
+                    bool off = key >= n || (CAUSAL && key > qrow);
+                    if constexpr (MODS) {
+                        off = off || (p.wr >= 0 && key > qrow + p.wr) || (p.wl >= 0 && key < qrow - p.wl);
+                        // slope (j - i) on the scaled score = slope / scale on the raw one
+                        s[b][kb2][r] = __builtin_fmaf(bias_coef, static_cast<float>(key - qrow), s[b][kb2][r]);
+                    }
                     s[b][kb2][r] = off ? -INFINITY : s[b][kb2][r];
                 }
             }
@@ -772,9 +791,24 @@ fa_fwd_kernel(Params p) {
     using Mask = std::integral_constant<bool, true>;
 
     // first tile that needs a mask (tail: n / BC; causal: (wrow0 + 1) / BC)
-    const int jm = (CAUSAL ? min(n / BC, (wrow0 + 1) / BC) : n / BC) - kt0;
+    // (windows: the right edge plays the diagonal's part, the left edge masks
+    // the first tiles, jh of them rounded up to a pair; a bias needs every
+    // tile to go through the mask step)
+    int jm = (CAUSAL ? min(n / BC, (wrow0 + 1) / BC) : n / BC) - kt0;
+    int jh = 0;
+    if constexpr (MODS) {
+        jm = (p.wr >= 0 ? min(n / BC, (wrow0 + p.wr + 1) / BC) : n / BC) - kt0;
+        if (p.wl >= 0) jh = max(0, (wrow0 + RW - 1 - p.wl - kt0 * BC + BC) / BC);
+        jh = (jh + 1) & ~1;
+        if (p.alibi) jm = -1;
+    }
     const int lim = min(nkv_w, jm);
     int j = 0;
+    // leading pairs whose next tiles a window's left edge cuts
+    for (; j + 1 < jh && j + 2 < nkv_w; j += 2) {
+        full_step(I0{}, Mask{}, sa, sb, j);
+        full_step(I1{}, Mask{}, sb, sa, j + 1);
+    }
     // hot loop: pairs of full steps whose next tiles need no mask
     for (; j + 2 < lim; j += 2) {
         full_step(I0{}, NoMask{}, sa, sb, j);
@@ -876,6 +910,12 @@ KernelFn select_exp(int expm, int rsm) {
         case FA_EXP_POLY: return select_rsm<D, CAUSAL, VARLEN, FA_EXP_POLY>(rsm);
         default: return select_rsm<D, CAUSAL, VARLEN, FA_EXP_MIXED>(rsm);
     }
+}
+
+template <int D>
+KernelFn select_mods() {
+    constexpr int BC = kTileKeys, NW = Geometry<D>::kWaves, QB = Geometry<D>::kBlocks;
+    return fa_fwd_kernel<D, BC, NW, QB, false, false, FA_EXP_HW, FA_RESCALE_THRESHOLD, false, true>;
 }
 
 template <int D>

@@ -9,4 +9,6 @@ KernelFn select_d128(bool causal, bool varlen, int exp_mode, int rescale_mode) {
 
 KernelFn select_split_d128(bool causal) { return select_split<128>(causal); }
 
+KernelFn select_mods_d128() { return select_mods<128>(); }
+
 }  // namespace fa_detail

@@ -9,4 +9,6 @@ KernelFn select_d256(bool causal, bool varlen, int exp_mode, int rescale_mode) {
 
 KernelFn select_split_d256(bool causal) { return select_split<256>(causal); }
 
+KernelFn select_mods_d256() { return select_mods<256>(); }
+
 }  // namespace fa_detail

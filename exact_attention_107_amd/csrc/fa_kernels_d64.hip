@@ -9,4 +9,6 @@ KernelFn select_d64(bool causal, bool varlen, int exp_mode, int rescale_mode) {
 
 KernelFn select_split_d64(bool causal) { return select_split<64>(causal); }
 
+KernelFn select_mods_d64() { return select_mods<64>(); }
+
 }  // namespace fa_detail

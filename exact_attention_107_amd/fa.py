@@ -21,7 +21,8 @@ EXP_HW, EXP_POLY, EXP_MIXED = 0, 1, 2
 RESCALE_ALWAYS, RESCALE_STRICT, RESCALE_THRESHOLD = 0, 1, 2
 EXPORTS = ("fa_fwd", "fa_fwd_variant", "fa_strerror", "fa_tile_rows", "fa_tile_keys",
            "fa_fwd_splitkv", "fa_merge", "fa_split_range", "fa_num_splits", "fa_bwd",
-           "fa_bwd_workspace_floats", "fa_fwd_fp8", "fa_quantize_fp8", "fa_fp8_vt_stride")
+           "fa_bwd_workspace_floats", "fa_fwd_fp8", "fa_quantize_fp8", "fa_fp8_vt_stride",
+           "fa_fwd_masked")
 
 _lib = None
 
@@ -72,6 +73,8 @@ def load(path: str | None = None):
     lib.fa_quantize_fp8.restype = i32
     lib.fa_fp8_vt_stride.argtypes = [i32]
     lib.fa_fp8_vt_stride.restype = i32
+    lib.fa_fwd_masked.argtypes = [vp] * 5 + [i32, i32, i32, i32, ctypes.c_float, i32, i32, vp, vp]
+    lib.fa_fwd_masked.restype = i32
     if path is None:
         _lib = lib
     return lib
@@ -378,6 +381,41 @@ def fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, vt8: torch.Tensor, descale_q: to
                             descale_k.data_ptr(), descale_v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                             B, H, N, d, ctypes.c_float(scale), int(bool(causal)),
                             ctypes.c_void_p(s.cuda_stream))
+    if rc != 0:
+        raise FaError(rc, strerror(rc))
+    return out, lse
+
+
+def fwd_masked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, window_left: int = -1,
+               window_right: int = -1, alibi_slopes: torch.Tensor | None = None,
+               scale: float | None = None, out: torch.Tensor | None = None,
+               lse: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None):
+    """``fa_fwd_masked``: window mask (``i - left <= j <= i + right``, negative =
+    unbounded) and optional per-head ALiBi slopes (fp32 ``[H]``), dense
+    ``[B, N, H, d]``.  Returns ``(o, lse)``."""
+    lib = load()
+    dev = q.device
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, name, torch.bfloat16, dev)
+    B, N, H, d = _dense_shape(q)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must have the same shape")
+    if alibi_slopes is not None:
+        _check(alibi_slopes, "alibi_slopes", torch.float32, dev)
+        if tuple(alibi_slopes.shape) != (H,):
+            raise ValueError(f"alibi_slopes must be [{H}]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if lse is None else lse
+    _check(out, "out", torch.bfloat16, dev)
+    _check(lse, "lse", torch.float32, dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = lib.fa_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                               B, H, N, d, ctypes.c_float(scale), int(window_left), int(window_right),
+                               alibi_slopes.data_ptr() if alibi_slopes is not None else None,
+                               ctypes.c_void_p(s.cuda_stream))
     if rc != 0:
         raise FaError(rc, strerror(rc))
     return out, lse

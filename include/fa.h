@@ -224,6 +224,26 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o,
 long long fa_bwd_workspace_floats(int B, int H, int N);
 
 /*
+ * fa_fwd_masked: fa_fwd with a window mask and an optional linear distance
+ * bias (dense layout) -- built-in forms of the score modifications and masks
+ * that FlexAttention user code expresses (FlashAttention-4 as a FlexAttention
+ * backend: "FlashAttention 1-4 explained", FlashAttention-4 section).
+ *   window_left, window_right   key j is visible to query i iff
+ *                  i - window_left <= j <= i + window_right; a negative value
+ *                  leaves that side unbounded (window_right = 0 with an
+ *                  unbounded left side is the causal mask).  Key tiles that
+ *                  no row of a workgroup sees are skipped.
+ *   alibi_slopes   NULL, or device fp32 [H]: slope_h * (j - i) is added to
+ *                  the scaled score (ALiBi).
+ * Every other argument as fa_fwd (no cu_seqlens, no causal flag).  Uses
+ * hardware exp and the threshold rescale; every tile goes through the mask.
+ */
+int fa_fwd_masked(const void *q, const void *k, const void *v, void *o,
+                  float *lse, int B, int H, int N, int d, float scale,
+                  int window_left, int window_right, const float *alibi_slopes,
+                  hipStream_t stream);
+
+/*
  * FP8 forward (dense layout, d = 64 or 128).  The FlashAttention-3 notes of
  * "FlashAttention 1-4 explained" run the forward's products on FP8 matrix
  * units; here Q K^T and P V both run on E4M3 operands (OCP E4M3: bias 7,

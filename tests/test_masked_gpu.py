@@ -1,0 +1,78 @@
+"""Window mask and linear distance bias (fa_fwd_masked), HIP path vs the
+oracle, through the C ABI (needs an MI355X).  Same tolerances as fa_fwd:
+the modifications change which scores enter the softmax and add an exact
+fp32 term to them, nothing else."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_107_amd import fa
+from exact_attention_107_amd.workloads import Run, make_inputs
+from gpu_helpers import assert_within, from_dev, metrics, to_dev
+from oracle import mods as omods
+
+pytestmark = pytest.mark.gpu
+
+
+def _alibi(H):
+    # the usual geometric slopes 2^(-8 (h + 1) / H)
+    return np.array([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], np.float32)
+
+
+def _run(inp, left, right, slopes):
+    q, k, v = (to_dev(inp[x]) for x in ("q", "k", "v"))
+    sl = torch.from_numpy(slopes).cuda() if slopes is not None else None
+    o, lse = fa.fwd_masked(q, k, v, window_left=left, window_right=right, alibi_slopes=sl, scale=inp["scale"])
+    torch.cuda.synchronize()
+    return o, lse
+
+
+WINDOWS = [(-1, 0), (128, 0), (100, 37), (0, 0), (-1, 200), (300, -1), (63, 64), (-1, -1)]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("window", WINDOWS, ids=lambda w: f"{w[0]}_{w[1]}")
+@pytest.mark.parametrize("bias", [False, True])
+def test_masked_small(d, window, bias):
+    inp = make_inputs(Run("mk", 1, 3, 700, d, False, 91))
+    slopes = _alibi(3) if bias else None
+    o, lse = _run(inp, *window, slopes)
+    ro, rl = omods.attention(inp["q"], inp["k"], inp["v"], scale=inp["scale"], left=window[0], right=window[1],
+                             slopes=slopes)
+    m = metrics(from_dev(o), lse.cpu().numpy(), ro, rl)
+    print(f"d={d} window={window} bias={bias} {m}")
+    assert_within(m, f"window={window} bias={bias}")
+
+
+def test_masked_d256_and_ragged_batch():
+    inp = make_inputs(Run("mk2", 2, 2, 333, 256, False, 92))
+    slopes = _alibi(2)
+    o, lse = _run(inp, 50, 10, slopes)
+    ro, rl = omods.attention(inp["q"], inp["k"], inp["v"], scale=inp["scale"], left=50, right=10, slopes=slopes)
+    assert_within(metrics(from_dev(o), lse.cpu().numpy(), ro, rl), "d=256")
+
+
+def test_masked_full_size_sampled():
+    """A long sliding-window causal run with ALiBi at benchmark size, on
+    sampled rows."""
+    inp = make_inputs(Run("mkl", 1, 16, 16384, 128, False, 93))
+    slopes = _alibi(16)
+    o, lse = _run(inp, 1024, 0, slopes)
+    rng = np.random.Generator(np.random.PCG64(3))
+    rows = np.array([(0, int(rng.integers(16)), i) for i in
+                     [0, 1, 1023, 1024, 1025, 8191, 16383] + list(rng.integers(0, 16384, 120))], dtype=np.int64)
+    ro, rl = omods.attention(inp["q"], inp["k"], inp["v"], scale=inp["scale"], left=1024, right=0, slopes=slopes,
+                             rows=rows)
+    rt = torch.from_numpy(rows)
+    og = from_dev(o[rt[:, 0].cuda(), rt[:, 2].cuda(), rt[:, 1].cuda()])
+    lg = lse[rt[:, 0].cuda(), rt[:, 1].cuda(), rt[:, 2].cuda()].cpu().numpy()
+    assert_within(metrics(og, lg, ro, rl), "sliding window 1024")
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+def test_masked_rejects_bad_arguments():
+    q = torch.zeros(1, 64, 1, 96, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fa.FaError):
+        fa.fwd_masked(q, q.clone(), q.clone(), window_left=4, window_right=0)
