@@ -68,6 +68,10 @@ constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
 // Threshold rescale: P~ = 2^(s*c - m) may reach 2^kTau before m moves.
 constexpr float kTau = 8.0f;
+// LDS fragment reads in flight ahead of the MFMA that uses them (K in the
+// score phase, V in the P V phase)
+constexpr int kKLookahead = 2;
+constexpr int kVLookahead = 2;
 
 
 // ---------------------------------------------------------------------------
@@ -620,21 +624,23 @@ fa_fwd_kernel(Params p) {
     // `work(m)` is VALU work placed after step m; it may produce pf[.][t] for a
     // later t.
     auto pv_run = [&](const char *vb, auto &&work) {
+        constexpr int LA = kVLookahead < MS ? kVLookahead : MS;  // fragments in flight
         bf16x8 vf[MS];
-        static_for<0, (MS < 2 ? MS : 2)>([&](auto m) {
+        static_for<0, LA>([&](auto m) {
             vf[m] = vfrag_issue(vb, std::integral_constant<int, m / NDB>{},
                                 std::integral_constant<int, m % NDB>{});
         });
         static_for<0, MS>([&](auto m) {
             constexpr int t = m / NDB, db = m % NDB;
-            if constexpr (m + 1 < MS) lgkm_wait<2>(vf[m]);
-            else lgkm_wait<0>(vf[m]);
+            // two LDS reads per fragment; the later fragments may stay in flight
+            constexpr int later = (LA - 1 < MS - 1 - m) ? LA - 1 : MS - 1 - m;
+            lgkm_wait<2 * later>(vf[m]);
 #pragma unroll
             for (int b = 0; b < QB; ++b)
                 oacc[b][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[m], pf[b][t], oacc[b][db], 0, 0, 0);
-            if constexpr (m + 2 < MS)
-                vf[m + 2] = vfrag_issue(vb, std::integral_constant<int, (m + 2) / NDB>{},
-                                        std::integral_constant<int, (m + 2) % NDB>{});
+            if constexpr (m + LA < MS)
+                vf[m + LA] = vfrag_issue(vb, std::integral_constant<int, (m + LA) / NDB>{},
+                                         std::integral_constant<int, (m + LA) % NDB>{});
             work(m);
         });
     };
@@ -659,16 +665,16 @@ fa_fwd_kernel(Params p) {
 #pragma unroll
             for (int i = 0; i < NKB; ++i) nxt[b][i] = f32x16{};
         }
-        bf16x8 kf[3];
+        constexpr int LA = kKLookahead < MS ? kKLookahead : MS;  // fragments in flight
+        bf16x8 kf[LA + 1];
         // step order alternates the NKB accumulator chains
-        kf[0] = kfrag(kb, 0, 0);
-        if constexpr (MS > 1) kf[1] = kfrag(kb, 1 / NKB, 1 % NKB);
+        static_for<0, LA>([&](auto i) { kf[i] = kfrag(kb, i / NKB, i % NKB); });
         static_for<0, MS>([&](auto m) {
             constexpr int kb2 = m % NKB, kk = m / NKB;
-            if constexpr (m + 2 < MS) kf[(m + 2) % 3] = kfrag(kb, (m + 2) / NKB, (m + 2) % NKB);
+            if constexpr (m + LA < MS) kf[(m + LA) % (LA + 1)] = kfrag(kb, (m + LA) / NKB, (m + LA) % NKB);
 #pragma unroll
             for (int b = 0; b < QB; ++b)
-                nxt[b][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[m % 3], qf[b][kk], nxt[b][kb2], 0, 0, 0);
+                nxt[b][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[m % (LA + 1)], qf[b][kk], nxt[b][kb2], 0, 0, 0);
             // elements [m*AE/MS, (m+1)*AE/MS) of the list (b, e), b-major
 #pragma unroll
             for (int x = m * AE / MS; x < (m + 1) * AE / MS; ++x) {
@@ -680,11 +686,11 @@ fa_fwd_kernel(Params p) {
         });
 #pragma unroll
         for (int b = 0; b < QB; ++b) anchor(rsum_a[b]);
-        __builtin_amdgcn_sched_group_barrier(0x100, MS > 1 ? 2 : 1, 0);  // first K fragments
+        __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);  // first K fragments
         static_for<0, MS>([&](auto m) {
             constexpr int ne = (m + 1) * AE / MS - m * AE / MS;  // elements of this step
             __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);  // MFMA
-            if constexpr (m + 2 < MS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+            if constexpr (m + LA < MS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
             if constexpr (ne > 0) __builtin_amdgcn_sched_group_barrier(0x402, 3 * ne + (ne + 1) / 2, 0);
         });
     };
@@ -767,7 +773,11 @@ fa_fwd_kernel(Params p) {
         issue_loads(j, (PAR ? k_lds1 : k_lds0), (PAR ? v_lds0 : v_lds1));
         if (rescale_o) o_rescale();
         __builtin_amdgcn_sched_barrier(0);
+        // the score MFMAs go first when the SIMD's two waves compete for
+        // issue (measured +1 %)
+        __builtin_amdgcn_s_setprio(1);
         phase_a(nxt, cur, (PAR ? k_lds0 : k_lds1));  // K_{j+1}
+        __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (decltype(mask)::value) s_mask(nxt, j + 1);
         float mx[QB];
