@@ -261,13 +261,41 @@ __device__ __forceinline__ bool decode_work(const Params &p, Work &w) {
         w.t0 = static_cast<long long>(w.b) * p.N;
         return true;
     } else {
-        // Items are (sequence, query tile) pairs ordered by query-tile index,
-        // highest first (for causal masks the work of a tile grows with its
-        // index); ties in sequence order.  Each wave decodes independently
-        // with ballots over up to 64 sequences at a time.
         const int lane = threadIdx.x & 63;
         w.h = wg % p.H;
         int r = wg / p.H;
+        if (p.B <= 64) {
+            // Items are ordered by sequence, longest first (ties by index),
+            // and within a sequence by query tile, highest first; the head
+            // varies fastest, so the tiles of one (sequence, head) run at
+            // about the same time on one XCD (wg % 8) and share its L2.
+            // Lane b computes where sequence b's tiles start in that order.
+            const int b = lane;
+            const int len = b < p.B ? p.cu[b + 1] - p.cu[b] : 0;
+            const int tiles = (len + BR - 1) / BR;
+            int pos = 0;
+            for (int o = 0; o < p.B; ++o) {
+                const int lo = p.cu[o + 1] - p.cu[o];
+                const bool before = lo > len || (lo == len && o < b);
+                pos += before ? (lo + BR - 1) / BR : 0;
+            }
+            const bool mine = b < p.B && r >= pos && r < pos + tiles;
+            const unsigned long long m = __ballot(mine);
+            if (m == 0) return false;  // surplus workgroup of the grid bound
+            const int bsel = __builtin_amdgcn_readfirstlane(__ffsll(static_cast<long long>(m)) - 1);
+            const int pos_sel = __builtin_amdgcn_readfirstlane(__shfl(pos, bsel));
+            const int tiles_sel = __builtin_amdgcn_readfirstlane(__shfl(tiles, bsel));
+            w.b = bsel;
+            w.qt = tiles_sel - 1 - (r - pos_sel);
+            const int s0 = __builtin_amdgcn_readfirstlane(p.cu[bsel]);
+            const int s1 = __builtin_amdgcn_readfirstlane(p.cu[bsel + 1]);
+            w.t0 = s0;
+            w.n = s1 - s0;
+            return true;
+        }
+        // More than 64 sequences: items ordered by query-tile index, highest
+        // first (for causal masks the work of a tile grows with its index),
+        // ties in sequence order; ballots over 64 sequences at a time.
         int lmax = 0;
         for (int base = 0; base < p.B; base += 64) {
             const int b = base + lane;
