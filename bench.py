@@ -170,23 +170,28 @@ def backward_run(torch, fa, name, steps=10, warmup=2):
     ri = make_inputs(r)
     q, k, v = (to_dev(ri[x], torch) for x in ("q", "k", "v"))
     do = to_dev(make_grad(ri["q"].shape, r.seed + 5000), torch)
-    o, lse = fa.fwd(q, k, v, causal=r.causal, scale=ri["scale"])
+    cu = None if ri["cu_seqlens"] is None else torch.from_numpy(ri["cu_seqlens"]).to("cuda")
+    o, lse = fa.fwd(q, k, v, causal=r.causal, scale=ri["scale"], cu_seqlens=cu)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    ws = torch.empty(fa.bwd_workspace_floats(r.B, r.H, r.N), dtype=torch.float32, device="cuda")
+    ws_floats = fa.bwd_workspace_floats(1, r.H, ri["T"]) if cu is not None else fa.bwd_workspace_floats(r.B, r.H, r.N)
+    ws = torch.empty(ws_floats, dtype=torch.float32, device="cuda")
 
     def launch():
-        fa.bwd(q, k, v, o, lse, do, causal=r.causal, scale=ri["scale"], dq=dq, dk=dk, dv=dv, workspace=ws)
+        fa.bwd(q, k, v, o, lse, do, causal=r.causal, scale=ri["scale"], cu_seqlens=cu, dq=dq, dk=dk, dv=dv,
+               workspace=ws)
 
     ms_step, ms, ms_med, ms_min = time_launches(launch, steps, warmup, torch)
     f = bwd_flops(ri["lengths"], r.H, r.d, r.causal)
     executed = f * 14.0 / 10.0
-    res = {"shape": f"B={r.B} H={r.H} N={r.N} d={r.d} causal={r.causal}", "ms": round(ms, 4),
+    shape = (f"{len(ri['lengths'])} packed sequences, T={ri['T']} H={r.H} d={r.d} causal={r.causal}"
+             if cu is not None else f"B={r.B} H={r.H} N={r.N} d={r.d} causal={r.causal}")
+    res = {"shape": shape, "ms": round(ms, 4),
            "ms_per_step": round(ms_step, 4), "tflops_credited": round(f / ms / 1e9, 1),
            "roofline": {"bound": "mfma", "achieved": round(executed / ms / 1e9, 1), "peak": PEAK_BF16_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(executed / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
                         "per_launch": "14*B*H*N^2*d executed MFMA flops (halved causal) / mean HIP-event "
                                       "duration of the three backward kernels"}}
-    del q, k, v, do, o, lse, dq, dk, dv, ws
+    del q, k, v, do, o, lse, dq, dk, dv, ws, cu
     return res, f, ms_step
 
 
@@ -400,7 +405,7 @@ def main() -> int:
         out["variants"] = variants
         out["split_kv"] = split_kv_runs(torch, fa)
         out["backward"] = {name: backward_run(torch, fa, name)[0]
-                           for name in ("mid", "mid_causal", "bwd_long", "bwd_long_causal")}
+                           for name in ("mid", "mid_causal", "bwd_long", "bwd_long_causal", "varlen_causal")}
         out["fp8"] = fp8_runs(torch, fa)
         out["masked"] = masked_runs(torch, fa)
 

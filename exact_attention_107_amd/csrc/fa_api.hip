@@ -252,12 +252,12 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
 
 long long fa_bwd_workspace_floats(int B, int H, int N) {
     if (B < 1 || H < 1 || N < 1) return 0;
-    return static_cast<long long>(B) * H * ((N + 31) / 32) * 64;
+    return 2LL * B * H * N;
 }
 
 int fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
            void *dq, void *dk, void *dv, int B, int H, int N, int d, float scale, int causal,
-           float *workspace, hipStream_t stream) {
+           const int32_t *cu_seqlens, float *workspace, hipStream_t stream) {
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return FA_ERR_NULLPTR;
     if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
@@ -265,12 +265,14 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const flo
     const void *t16[] = {q, k, v, o, dout, dq, dk, dv, workspace};
     for (const void *t : t16)
         if (misaligned(t, 16)) return FA_ERR_ALIGN;
-    if (misaligned(lse, 4)) return FA_ERR_ALIGN;
-    const long long rows = static_cast<long long>(B) * N * H;
+    if (misaligned(lse, 4) || misaligned(cu_seqlens, 4)) return FA_ERR_ALIGN;
+    const bool packed = cu_seqlens != nullptr;
+    const long long tokens = packed ? static_cast<long long>(N) : static_cast<long long>(B) * N;
+    const long long rows = tokens * H;
     const long long elems = rows * d;
     if (elems <= 0 || elems > (1LL << 46) || !token_stride_ok(H, d)) return FA_ERR_SHAPE;
     const size_t tb = static_cast<size_t>(elems) * 2, lb = static_cast<size_t>(rows) * 4;
-    const size_t wb = static_cast<size_t>(fa_bwd_workspace_floats(B, H, N)) * 4;
+    const size_t wb = static_cast<size_t>(rows) * 8;  // two floats per LSE entry
     const void *outs[] = {dq, dk, dv, workspace};
     const size_t out_bytes[] = {tb, tb, tb, wb};
     const void *ins[] = {q, k, v, o, dout, lse};
@@ -289,6 +291,7 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const flo
     bp.o = static_cast<const uint16_t *>(o);
     bp.dout = static_cast<const uint16_t *>(dout);
     bp.lse = lse;
+    bp.cu = cu_seqlens;
     bp.dq = static_cast<uint16_t *>(dq);
     bp.dk = static_cast<uint16_t *>(dk);
     bp.dv = static_cast<uint16_t *>(dv);
@@ -296,13 +299,15 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const flo
     bp.B = B;
     bp.H = H;
     bp.N = N;
-    bp.nqb = (N + 31) / 32;
     bp.cs = scale * kLog2e;
     bp.scale = scale;
-    const BwdKernels ks = d == 64 ? select_bwd_d64(causal != 0) : select_bwd_d128(causal != 0);
-    const long long prep_grid = (static_cast<long long>(B) * H * bp.nqb * 32 + 255) / 256;
-    const long long kv_grid = static_cast<long long>(B) * H * ((N + 127) / 128);
-    const long long q_grid = static_cast<long long>(B) * H * ((N + 127) / 128);
+    const BwdKernels ks = d == 64 ? select_bwd_d64(causal != 0, packed) : select_bwd_d128(causal != 0, packed);
+    // key tiles of the dK/dV kernel and query tiles of the dQ kernel: 128
+    // each; packed: a bound on sum_b ceil(n_b / 128), surplus workgroups exit
+    const long long tiles = (static_cast<long long>(N) + 127) / 128;
+    const long long prep_grid = (rows + 255) / 256;
+    const long long kv_grid = packed ? static_cast<long long>(H) * (tiles + B) : static_cast<long long>(B) * H * tiles;
+    const long long q_grid = kv_grid;
     if (prep_grid > 0x7fffffffLL || kv_grid > 0x7fffffffLL || q_grid > 0x7fffffffLL) return FA_ERR_SHAPE;
     (void)hipGetLastError();
     hipLaunchKernelGGL(ks.prep, dim3(static_cast<unsigned>(prep_grid)), dim3(256), 0, stream, bp);

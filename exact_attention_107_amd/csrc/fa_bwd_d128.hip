@@ -3,6 +3,6 @@
 
 namespace fa_detail {
 
-BwdKernels select_bwd_d128(bool causal) { return select_bwd<128>(causal); }
+BwdKernels select_bwd_d128(bool causal, bool packed) { return select_bwd<128>(causal, packed); }
 
 }  // namespace fa_detail

@@ -3,6 +3,6 @@
 
 namespace fa_detail {
 
-BwdKernels select_bwd_d64(bool causal) { return select_bwd<64>(causal); }
+BwdKernels select_bwd_d64(bool causal, bool packed) { return select_bwd<64>(causal, packed); }
 
 }  // namespace fa_detail

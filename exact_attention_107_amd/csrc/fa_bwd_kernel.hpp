@@ -13,9 +13,8 @@
 //
 // Three kernels, none with atomics, so every result is bitwise reproducible
 // (the deterministic mode of section 3.3 of the V4 explainer):
-//  * prep: delta and LSE * log2(e) per query row, stored per block of 32
-//    rows as [32 x LSE*log2e | 32 x delta] (rows past the sequence get +inf
-//    and 0, which makes their P exactly 0 below).
+//  * prep: delta and LSE * log2(e) per query row, stored as a pair at the
+//    row's LSE index (dense [B, H, N] or packed [H, T]).
 //  * dK/dV: a workgroup owns 128 keys (32 per wave) and walks over the query
 //    blocks; dK^T and dV^T accumulate in registers.  S = Q K^T and dP = dO V^T
 //    put one key per lane, so P and dS, converted to bf16 in place, are
@@ -31,6 +30,11 @@
 // chunks are XOR-permuted by sg(r): a row read (16 lanes, 16 rows, one
 // chunk) and a transposed read (32 lanes, 4 rows x 4 chunks) both touch 16
 // distinct bank groups.
+//
+// Packed sequences (cu_seqlens, the layout of the packed forward): every
+// sequence is its own attention problem; a workgroup's tile is counted from
+// its sequence's first token, loads are clipped at the sequence end and the
+// masks use the sequence's length.
 
 #pragma once
 
@@ -141,43 +145,117 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // ---------------------------------------------------------------------------
-// prep: delta_i = sum_d dO_id O_id and LSE_i * log2(e), per 32-row block.
+// prep: delta_i = sum_d dO_id O_id and LSE_i * log2(e), one thread per LSE
+// entry t, stored as the pair stats[2 t], stats[2 t + 1].
 
 template <int D>
 __global__ void __launch_bounds__(256) fa_bwd_prep_kernel(BwdParams p) {
     const long long t = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
-    const long long per_bh = static_cast<long long>(p.nqb) * 32;
-    if (t >= per_bh * p.B * p.H) return;
-    const long long bh = t / per_bh;
-    const int i = static_cast<int>(t - bh * per_bh);
-    const int b = static_cast<int>(bh / p.H), h = static_cast<int>(bh - static_cast<long long>(b) * p.H);
-    float lse2 = INFINITY, delta = 0.0f;
-    if (i < p.N) {
-        const long long base = ((static_cast<long long>(b) * p.N + i) * p.H + h) * D;
-        const u32x4 *dq = reinterpret_cast<const u32x4 *>(p.dout + base);
-        const u32x4 *oq = reinterpret_cast<const u32x4 *>(p.o + base);
-        float acc = 0.0f;
-#pragma unroll
-        for (int cch = 0; cch < D / 8; ++cch) {
-            const u32x4 a = dq[cch], o = oq[cch];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                acc = __builtin_fmaf(bf16_lo(a[w]), bf16_lo(o[w]), acc);
-                acc = __builtin_fmaf(bf16_hi(a[w]), bf16_hi(o[w]), acc);
-            }
-        }
-        delta = acc;
-        lse2 = p.lse[bh * p.N + i] * kLog2e;
+    const long long rows = static_cast<long long>(p.cu ? 1 : p.B) * p.H * p.N;
+    if (t >= rows) return;
+    // token and head of LSE entry t: packed [H, T], dense [B, H, N]
+    long long tok;
+    int h;
+    if (p.cu) {
+        h = static_cast<int>(t / p.N);
+        tok = t - static_cast<long long>(h) * p.N;
+    } else {
+        const long long bh = t / p.N;
+        const int b = static_cast<int>(bh / p.H);
+        h = static_cast<int>(bh - static_cast<long long>(b) * p.H);
+        tok = static_cast<long long>(b) * p.N + (t - bh * p.N);
     }
-    float *s = p.stats + (bh * p.nqb + i / 32) * 64;
-    s[i % 32] = lse2;
-    s[32 + i % 32] = delta;
+    const long long base = (tok * p.H + h) * D;
+    const u32x4 *dq = reinterpret_cast<const u32x4 *>(p.dout + base);
+    const u32x4 *oq = reinterpret_cast<const u32x4 *>(p.o + base);
+    float acc = 0.0f;
+#pragma unroll
+    for (int cch = 0; cch < D / 8; ++cch) {
+        const u32x4 a = dq[cch], o = oq[cch];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            acc = __builtin_fmaf(bf16_lo(a[w]), bf16_lo(o[w]), acc);
+            acc = __builtin_fmaf(bf16_hi(a[w]), bf16_hi(o[w]), acc);
+        }
+    }
+    const u32x2 st = {__float_as_uint(p.lse[t] * kLog2e), __float_as_uint(acc)};
+    *reinterpret_cast<u32x2 *>(p.stats + 2 * t) = st;
+}
+
+// ---------------------------------------------------------------------------
+// Work items: head h and tile `tile` (of TILE keys or rows, counted from the
+// first token of the sequence) of one sequence of length n starting at token
+// t0; lrow is the LSE index of the sequence's first row for head h.
+
+struct BwdItem {
+    int h, tile, n;
+    long long t0, lrow;
+};
+
+// Packed sequences: items are ordered by sequence and, within it, by tile,
+// with the head varying fastest (the tiles of one sequence and head run at
+// about the same time, on one XCD).  Up to 64 sequences the longest go
+// first; beyond that they keep their order.  HIGH_FIRST numbers a
+// sequence's tiles from its end.  Returns false for a surplus workgroup of
+// the grid bound H * (ceil(T / TILE) + B).
+template <int TILE, bool HIGH_FIRST>
+__device__ __forceinline__ bool bwd_packed_item(const BwdParams &p, BwdItem &it) {
+    const int lane = threadIdx.x & 63;
+    const int r = static_cast<int>(blockIdx.x) / p.H;
+    it.h = static_cast<int>(blockIdx.x) - r * p.H;
+    int sel = -1, local = 0, tiles_sel = 0;
+    if (p.B <= 64) {
+        // lane b: where sequence b's tiles start when longer sequences (ties:
+        // lower index) come first
+        const int b = lane;
+        const int len = b < p.B ? p.cu[b + 1] - p.cu[b] : 0;
+        const int tiles = (len + TILE - 1) / TILE;
+        int pos = 0;
+        for (int o = 0; o < p.B; ++o) {
+            const int lo = p.cu[o + 1] - p.cu[o];
+            pos += (lo > len || (lo == len && o < b)) ? (lo + TILE - 1) / TILE : 0;
+        }
+        const unsigned long long m = __ballot(b < p.B && r >= pos && r < pos + tiles);
+        if (m == 0) return false;
+        sel = __builtin_amdgcn_readfirstlane(__ffsll(static_cast<long long>(m)) - 1);
+        local = r - __builtin_amdgcn_readfirstlane(__shfl(pos, sel));
+        tiles_sel = __builtin_amdgcn_readfirstlane(__shfl(tiles, sel));
+    } else {
+        int pos = 0;  // tiles of the sequences before this chunk of 64
+        for (int c0 = 0; c0 < p.B; c0 += 64) {
+            const int b = c0 + lane;
+            const int tiles = b < p.B ? (p.cu[b + 1] - p.cu[b] + TILE - 1) / TILE : 0;
+            int incl = tiles;  // inclusive prefix sum over the lanes
+            for (int off = 1; off < 64; off <<= 1) {
+                const int x = __shfl_up(incl, off);
+                if (lane >= off) incl += x;
+            }
+            const int total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+            if (r < pos + total) {
+                const unsigned long long m = __ballot(r >= pos + incl - tiles && r < pos + incl);
+                const int l = __builtin_amdgcn_readfirstlane(__ffsll(static_cast<long long>(m)) - 1);
+                sel = c0 + l;
+                local = r - pos - __builtin_amdgcn_readfirstlane(__shfl(incl - tiles, l));
+                tiles_sel = __builtin_amdgcn_readfirstlane(__shfl(tiles, l));
+                break;
+            }
+            pos += total;
+        }
+        if (sel < 0) return false;
+    }
+    it.tile = HIGH_FIRST ? tiles_sel - 1 - local : local;
+    const int s0 = __builtin_amdgcn_readfirstlane(p.cu[sel]);
+    const int s1 = __builtin_amdgcn_readfirstlane(p.cu[sel + 1]);
+    it.t0 = s0;
+    it.n = s1 - s0;
+    it.lrow = static_cast<long long>(it.h) * p.N + s0;
+    return true;
 }
 
 // ---------------------------------------------------------------------------
 // dK, dV: workgroup = (b, h, key tile of 128 keys).
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PACKED>
 __global__ void __launch_bounds__(kBwdWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 fa_bwd_dkdv_kernel(BwdParams p) {
     constexpr int NW = kBwdWaves, KW = kBwdKeysPerWave, BK = kBwdKeyTile, BQ = kBwdQBlock;
@@ -191,24 +269,35 @@ fa_bwd_dkdv_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(1024))) char v_lds[VT];
     __shared__ __attribute__((aligned(256))) float st_lds0[64], st_lds1[64];
 
-    const int BH = p.B * p.H;
-    const int n = p.N;
-    const int n_kt = (n + BK - 1) / BK;
-    int bh, kt;
-    if constexpr (CAUSAL) {
-        // low key tiles see the most query blocks: they go first
-        kt = blockIdx.x / BH;
-        bh = blockIdx.x - kt * BH;
+    BwdItem it;
+    if constexpr (PACKED) {
+        // causal: a sequence's low key tiles see the most query blocks
+        if (!bwd_packed_item<BK, false>(p, it)) return;
     } else {
-        // each XCD (blockIdx % 8) takes a contiguous run of items, so the key
-        // tiles of one (b, h) share that XCD's L2 for their Q and dO stream
-        const int G = gridDim.x, x = blockIdx.x & 7, sx = blockIdx.x >> 3;
-        const int per = G >> 3, rem = G & 7;
-        const int item = x * per + (x < rem ? x : rem) + sx;
-        bh = item / n_kt;
-        kt = item - bh * n_kt;
+        const int BH = p.B * p.H;
+        const int n_kt = (p.N + BK - 1) / BK;
+        int bh, kt;
+        if constexpr (CAUSAL) {
+            // low key tiles see the most query blocks: they go first
+            kt = blockIdx.x / BH;
+            bh = blockIdx.x - kt * BH;
+        } else {
+            // each XCD (blockIdx % 8) takes a contiguous run of items, so the key
+            // tiles of one (b, h) share that XCD's L2 for their Q and dO stream
+            const int G = gridDim.x, x = blockIdx.x & 7, sx = blockIdx.x >> 3;
+            const int per = G >> 3, rem = G & 7;
+            const int item = x * per + (x < rem ? x : rem) + sx;
+            bh = item / n_kt;
+            kt = item - bh * n_kt;
+        }
+        const int b = bh / p.H;
+        it.h = bh - b * p.H;
+        it.tile = kt;
+        it.n = p.N;
+        it.t0 = static_cast<long long>(b) * p.N;
+        it.lrow = static_cast<long long>(bh) * p.N;
     }
-    const int b = bh / p.H, h = bh - b * p.H;
+    const int n = it.n, kt = it.tile, h = it.h;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 31, hh = lane >> 5;
@@ -216,7 +305,7 @@ fa_bwd_dkdv_kernel(BwdParams p) {
     const int kw0 = j0 + wave * KW;  // this wave's first key
     const long long rs = static_cast<long long>(p.H) * D;
     const int rs_bytes = static_cast<int>(rs) * 2;
-    const long long base = (static_cast<long long>(b) * n * p.H + h) * D;  // token 0 of (b, h)
+    const long long base = (it.t0 * p.H + h) * D;  // token 0 of the sequence, head h
 
     // K of this wave's keys, B operand of S = Q K^T: lane (c, hh) holds
     // K[kw0 + c][16 ks + 8 hh .. +8]; keys >= n read as zeros.
@@ -233,11 +322,14 @@ fa_bwd_dkdv_kernel(BwdParams p) {
     ad.init(lane);
     const int qvoff = QDMA::voff(wave, lane, rs_bytes);
     const int vvoff = VDMA::voff(wave, lane, rs_bytes);
-    const float *stats_bh = p.stats + static_cast<long long>(bh) * p.nqb * 64;
+    // (LSE*log2e, delta) pairs of the sequence's rows; lane l < 32 fetches
+    // row l's LSE, lane 32 + l its delta: st_lds = [32 x LSE*log2e | 32 x delta]
+    const float *stats_seq = p.stats + 2 * it.lrow;
+    const int st_off = lane < 32 ? lane * 8 : (lane - 32) * 8 + 4;
 
     // query blocks: causal starts at the tile's first key
     const int qb0 = CAUSAL ? j0 / BQ : 0;
-    const int nqb = p.nqb;
+    const int nqb = (n + BQ - 1) / BQ;
     auto dma_block = [&](int qb, char *qd, char *dd, float *sd) __attribute__((always_inline)) {
         const int q0 = qb * BQ;
         const auto qrs = make_rsrc(p.q + base + q0 * rs, (long long)(n - q0) * rs_bytes);
@@ -245,8 +337,9 @@ fa_bwd_dkdv_kernel(BwdParams p) {
         const auto drs = make_rsrc(p.dout + base + q0 * rs, (long long)(n - q0) * rs_bytes);
         QDMA::load(drs, dd, wave, qvoff, rs_bytes);
         if (wave == 0) {
-            const auto srs = make_rsrc(stats_bh + qb * 64, 256);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, LDS_PTR(void, sd), 4, lane * 4, 0, 0, 0);
+            // rows past the sequence read (0, 0); the mask gives them P = 0
+            const auto srs = make_rsrc(stats_seq + 2 * q0, (long long)(n - q0) * 8);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, LDS_PTR(void, sd), 4, st_off, 0, 0, 0);
         }
     };
     {
@@ -308,7 +401,9 @@ fa_bwd_dkdv_kernel(BwdParams p) {
                         float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], cs, -l4[r]));
                         if constexpr (MASK) {
                             const int key = kw0 + c, qry = q0 + 8 * g + 4 * hh + r;
-                            const bool off = key >= n || (CAUSAL && key > qry);
+                            // (query rows past the sequence: P = 0 whatever the
+                            // tile's rows past it hold)
+                            const bool off = key >= n || qry >= n || (CAUSAL && key > qry);
                             pe = off ? 0.0f : pe;
                         }
                         pv[r] = pe;
@@ -362,7 +457,7 @@ fa_bwd_dkdv_kernel(BwdParams p) {
         const int q0 = qb * BQ;
         // causal: queries q0 .. q0+31 all precede this wave's keys -> nothing
         if (!CAUSAL || q0 + BQ - 1 >= kw0) {
-            block(qcur, dcur, scur, q0, key_tail || (CAUSAL && q0 < kw0 + KW));
+            block(qcur, dcur, scur, q0, key_tail || q0 + BQ > n || (CAUSAL && q0 < kw0 + KW));
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -398,7 +493,7 @@ fa_bwd_dkdv_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dQ: workgroup = (b, h, query tile of 128 rows), like the forward.
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PACKED>
 __global__ void __launch_bounds__(kBwdWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 fa_bwd_dq_kernel(BwdParams p) {
     constexpr int NW = kBwdWaves, BR = kBwdQTile, BC = kBwdKvTile;
@@ -408,21 +503,32 @@ fa_bwd_dq_kernel(BwdParams p) {
 
     __shared__ __attribute__((aligned(1024))) char k_lds0[TT], k_lds1[TT], v_lds0[TT], v_lds1[TT];
 
-    const int BH = p.B * p.H;
-    const int n = p.N;
-    const int n_qt = (n + BR - 1) / BR;
-    int bh, qt;
-    if constexpr (CAUSAL) {
-        qt = n_qt - 1 - static_cast<int>(blockIdx.x) / BH;  // longest first
-        bh = blockIdx.x - (n_qt - 1 - qt) * BH;
+    BwdItem it;
+    if constexpr (PACKED) {
+        // causal: a sequence's high query tiles see the most keys
+        if (!bwd_packed_item<BR, CAUSAL>(p, it)) return;
     } else {
-        const int G = gridDim.x, x = blockIdx.x & 7, sx = blockIdx.x >> 3;
-        const int per = G >> 3, rem = G & 7;
-        const int item = x * per + (x < rem ? x : rem) + sx;
-        bh = item / n_qt;
-        qt = item - bh * n_qt;
+        const int BH = p.B * p.H;
+        const int n_qt = (p.N + BR - 1) / BR;
+        int bh, qt;
+        if constexpr (CAUSAL) {
+            qt = n_qt - 1 - static_cast<int>(blockIdx.x) / BH;  // longest first
+            bh = blockIdx.x - (n_qt - 1 - qt) * BH;
+        } else {
+            const int G = gridDim.x, x = blockIdx.x & 7, sx = blockIdx.x >> 3;
+            const int per = G >> 3, rem = G & 7;
+            const int item = x * per + (x < rem ? x : rem) + sx;
+            bh = item / n_qt;
+            qt = item - bh * n_qt;
+        }
+        const int b = bh / p.H;
+        it.h = bh - b * p.H;
+        it.tile = qt;
+        it.n = p.N;
+        it.t0 = static_cast<long long>(b) * p.N;
+        it.lrow = static_cast<long long>(bh) * p.N;
     }
-    const int b = bh / p.H, h = bh - b * p.H;
+    const int n = it.n, qt = it.tile, h = it.h;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 31, hh = lane >> 5;
@@ -430,7 +536,7 @@ fa_bwd_dq_kernel(BwdParams p) {
     const int wrow0 = q0 + wave * 32;
     const long long rs = static_cast<long long>(p.H) * D;
     const int rs_bytes = static_cast<int>(rs) * 2;
-    const long long base = (static_cast<long long>(b) * n * p.H + h) * D;
+    const long long base = (it.t0 * p.H + h) * D;
 
     // Q and dO of this wave's rows, B operands of S^T = K Q^T, dP^T = V dO^T
     bf16x8 qf[KK], df[KK];
@@ -444,12 +550,12 @@ fa_bwd_dq_kernel(BwdParams p) {
             df[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(drs, vo + ks * 32, 0, 0));
         }
     }
-    // this lane's query row: LSE * log2(e) and delta; rows past n (whose
-    // 32-row block may lie past the statistics) take +inf and 0, so P = 0
+    // this lane's query row: LSE * log2(e) and delta; rows past n take +inf
+    // and 0, so their P = 0
     const bool row_ok = wrow0 + c < n;
-    const float *st = p.stats + (static_cast<long long>(bh) * p.nqb + min(wrow0 / 32, p.nqb - 1)) * 64;
-    const float lse2 = row_ok ? st[c] : INFINITY;
-    const float delta = row_ok ? st[32 + c] : 0.0f;
+    const float *st = p.stats + 2 * (it.lrow + (row_ok ? wrow0 + c : 0));
+    const float lse2 = row_ok ? st[0] : INFINITY;
+    const float delta = row_ok ? st[1] : 0.0f;
 
     BwdAddr<D> ad;
     ad.init(lane);
@@ -561,9 +667,13 @@ fa_bwd_dq_kernel(BwdParams p) {
 }
 
 template <int D>
-BwdKernels select_bwd(bool causal) {
-    if (causal) return {fa_bwd_prep_kernel<D>, fa_bwd_dkdv_kernel<D, true>, fa_bwd_dq_kernel<D, true>};
-    return {fa_bwd_prep_kernel<D>, fa_bwd_dkdv_kernel<D, false>, fa_bwd_dq_kernel<D, false>};
+BwdKernels select_bwd(bool causal, bool packed) {
+    if (packed) {
+        if (causal) return {fa_bwd_prep_kernel<D>, fa_bwd_dkdv_kernel<D, true, true>, fa_bwd_dq_kernel<D, true, true>};
+        return {fa_bwd_prep_kernel<D>, fa_bwd_dkdv_kernel<D, false, true>, fa_bwd_dq_kernel<D, false, true>};
+    }
+    if (causal) return {fa_bwd_prep_kernel<D>, fa_bwd_dkdv_kernel<D, true, false>, fa_bwd_dq_kernel<D, true, false>};
+    return {fa_bwd_prep_kernel<D>, fa_bwd_dkdv_kernel<D, false, false>, fa_bwd_dq_kernel<D, false, false>};
 }
 
 }  // namespace fa_detail

@@ -96,13 +96,13 @@ int launch_merge(const MergeParams &mp, int d, void *stream);
 
 // Backward pass (fa_bwd_kernel.hpp).
 struct BwdParams {
-    const uint16_t *q, *k, *v, *o, *dout;  // bf16 [B, N, H, d]
-    const float *lse;                      // [B, H, N], natural log
-    uint16_t *dq, *dk, *dv;                // bf16 [B, N, H, d]
-    float *stats;                          // [B, H, nqb, 64]: per 32-row block,
-                                           // 32 x LSE*log2(e) then 32 x delta
-    int B, H, N;
-    int nqb;                               // ceil(N / 32)
+    const uint16_t *q, *k, *v, *o, *dout;  // bf16 [B, N, H, d], packed [T, H, d]
+    const float *lse;                      // [B, H, N], packed [H, T]; natural log
+    const int32_t *cu;                     // packed: sequence offsets [B + 1]; dense: null
+    uint16_t *dq, *dk, *dv;                // bf16, layout of q
+    float *stats;                          // two floats per LSE entry, same index:
+                                           // LSE*log2(e), delta
+    int B, H, N;                           // packed: B sequences, N = T tokens
     float cs;                              // scale * log2(e)
     float scale;
 };
@@ -110,8 +110,8 @@ using BwdKernelFn = void (*)(BwdParams);
 struct BwdKernels {
     BwdKernelFn prep, dkdv, dq;
 };
-BwdKernels select_bwd_d64(bool causal);
-BwdKernels select_bwd_d128(bool causal);
+BwdKernels select_bwd_d64(bool causal, bool packed);
+BwdKernels select_bwd_d128(bool causal, bool packed);
 
 // FP8 (E4M3) forward and quantisation (fa_fp8_kernel.hpp).
 struct Fp8Params {

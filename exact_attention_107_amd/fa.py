@@ -63,7 +63,7 @@ def load(path: str | None = None):
     lib.fa_split_range.restype = i32
     lib.fa_num_splits.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.fa_num_splits.restype = i32
-    lib.fa_bwd.argtypes = [vp] * 9 + [i32, i32, i32, i32, ctypes.c_float, i32, vp, vp]
+    lib.fa_bwd.argtypes = [vp] * 9 + [i32, i32, i32, i32, ctypes.c_float, i32, vp, vp, vp]
     lib.fa_bwd.restype = i32
     lib.fa_bwd_workspace_floats.argtypes = [i32, i32, i32]
     lib.fa_bwd_workspace_floats.restype = ctypes.c_longlong
@@ -188,7 +188,7 @@ def num_splits(B: int, H: int, N: int, d: int, causal: bool = False, num_cus: in
 
 def _dense_shape(q):
     if q.dim() != 4:
-        raise ValueError("split-KV tensors are dense [B, N, H, d]")
+        raise ValueError("dense tensors are [B, N, H, d]")
     return tuple(int(x) for x in q.shape)
 
 
@@ -273,27 +273,40 @@ def bwd_workspace_floats(B: int, H: int, N: int) -> int:
 
 def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
         dout: torch.Tensor, *, causal: bool = False, scale: float | None = None,
+        cu_seqlens: torch.Tensor | None = None,
         dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
         dv: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
         stream: torch.cuda.Stream | None = None):
-    """Gradients of the attention forward (``fa_bwd``), dense ``[B, N, H, d]``.
+    """Gradients of the attention forward (``fa_bwd``).
 
-    ``o`` and ``lse`` are the forward's outputs, ``dout`` the upstream
-    gradient.  Returns ``(dq, dk, dv)`` (bf16, shaped like q); the fp32
-    workspace is allocated with torch unless given.
+    Layouts as ``fwd``: dense ``[B, N, H, d]`` with ``lse [B, H, N]``, or
+    packed ``[T, H, d]`` with ``cu_seqlens`` (int32 ``[B+1]``) and
+    ``lse [H, T]``.  ``o`` and ``lse`` are the forward's outputs, ``dout``
+    the upstream gradient.  Returns ``(dq, dk, dv)`` (bf16, shaped like q);
+    the fp32 workspace is allocated with torch unless given.
     """
     lib = load()
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("q must be a GPU tensor")
-    B, N, H, d = _dense_shape(q)
+    if cu_seqlens is None:
+        B, N, H, d = _dense_shape(q)
+        lse_shape, ws_batch, cu_ptr = (B, H, N), B, None
+    else:
+        _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        if q.dim() != 3 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("packed q must be [T, H, d] with cu_seqlens [B+1]")
+        N, H, d = q.shape
+        B = cu_seqlens.numel() - 1
+        lse_shape, ws_batch, cu_ptr = (H, N), 1, cu_seqlens.data_ptr()
+    shape = tuple(q.shape)
     for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
         _check(t, name, torch.bfloat16, dev)
-        if tuple(t.shape) != (B, N, H, d):
-            raise ValueError(f"{name} must be {(B, N, H, d)}")
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be {shape}")
     _check(lse, "lse", torch.float32, dev)
-    if tuple(lse.shape) != (B, H, N):
-        raise ValueError(f"lse must be {(B, H, N)}")
+    if tuple(lse.shape) != lse_shape:
+        raise ValueError(f"lse must be {lse_shape}")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = torch.empty_like(q) if dq is None else dq
@@ -301,9 +314,9 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse:
     dv = torch.empty_like(v) if dv is None else dv
     for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
         _check(t, name, torch.bfloat16, dev)
-        if tuple(t.shape) != (B, N, H, d):
-            raise ValueError(f"{name} must be {(B, N, H, d)}")
-    wf = bwd_workspace_floats(B, H, N)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be {shape}")
+    wf = bwd_workspace_floats(ws_batch, H, N)
     if workspace is None:
         workspace = torch.empty(wf, dtype=torch.float32, device=dev)
     _check(workspace, "workspace", torch.float32, dev)
@@ -312,9 +325,9 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse:
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
         rc = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                        dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
-                        ctypes.c_float(scale), int(bool(causal)), workspace.data_ptr(),
-                        ctypes.c_void_p(s.cuda_stream))
+                        dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), int(B), int(H),
+                        int(N), int(d), ctypes.c_float(scale), int(bool(causal)), cu_ptr,
+                        workspace.data_ptr(), ctypes.c_void_p(s.cuda_stream))
     if rc != 0:
         raise FaError(rc, strerror(rc))
     return dq, dk, dv

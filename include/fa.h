@@ -193,7 +193,7 @@ int fa_split_range(int N, int d, int causal, int num_splits, int s, int row,
 int fa_num_splits(int B, int H, int N, int d, int causal, int num_cus);
 
 /*
- * fa_bwd: gradients of exact attention (dense layout only, d = 64 or 128).
+ * fa_bwd: gradients of exact attention (d = 64 or 128), dense or packed.
  * For the forward O = softmax(scale Q K^T) V and an upstream gradient dO it
  * writes
  *     dV = P^T dO,  dQ = scale dS K,  dK = scale dS^T Q,
@@ -203,12 +203,18 @@ int fa_num_splits(int B, int H, int N, int d, int causal, int num_cus);
  * of "FlashAttention 1-4 explained").  No atomics are used: results are
  * bitwise reproducible run to run (the deterministic mode of section 3.3 of
  * "Understanding FlashAttention V4").
- *   q, k, v, o, dout  device bf16 [B, N, H, d]: the forward's inputs, its
+ *   q, k, v, o, dout  device bf16, the forward's layout: [B, N, H, d], or
+ *                     [T, H, d] with cu_seqlens: the forward's inputs, its
  *                     output O and the upstream gradient dO.
- *   lse               device fp32 [B, H, N]: the forward's LSE.
- *   dq, dk, dv        device bf16 outputs [B, N, H, d].
- *   workspace         device fp32 scratch of fa_bwd_workspace_floats(B, H, N)
- *                     floats (16-byte aligned); overwritten.
+ *   lse               device fp32, the forward's LSE: [B, H, N] or [H, T].
+ *   dq, dk, dv        device bf16 outputs in the layout of q.
+ *   cu_seqlens        as fa_fwd: NULL (dense) or device int32 [B + 1]
+ *                     sequence offsets, N = T; each sequence is its own
+ *                     attention problem.
+ *   workspace         device fp32 scratch of two floats per LSE entry,
+ *                     fa_bwd_workspace_floats(B, H, N) dense and
+ *                     fa_bwd_workspace_floats(1, H, T) packed (16-byte
+ *                     aligned); overwritten.
  *   B, H, N, scale, causal, stream   as fa_fwd.
  * Three kernels are queued on `stream`.  Outputs and the workspace must not
  * overlap any input or each other.  Errors as fa_fwd; FA_ERR_HEAD_DIM for
@@ -217,10 +223,10 @@ int fa_num_splits(int B, int H, int N, int d, int causal, int num_cus);
 int fa_bwd(const void *q, const void *k, const void *v, const void *o,
            const float *lse, const void *dout, void *dq, void *dk, void *dv,
            int B, int H, int N, int d, float scale, int causal,
-           float *workspace, hipStream_t stream);
+           const int32_t *cu_seqlens, float *workspace, hipStream_t stream);
 
-/* Size of fa_bwd's workspace in floats: B * H * ceil(N / 32) * 64 (0 for an
- * invalid shape). */
+/* Size of fa_bwd's workspace in floats: 2 * B * H * N (0 for an invalid
+ * shape); for packed sequences pass B = 1 and N = T. */
 long long fa_bwd_workspace_floats(int B, int H, int N);
 
 /*

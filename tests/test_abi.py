@@ -206,9 +206,10 @@ DQ, DK, DV, DO, WS = 0x30000000, 0x40000000, 0x50000000, 0x60000000, 0x70000000
 
 
 def call_bwd(lib, q=Q, k=K, v=V, o=O, lse=L, do=DO, dq=DQ, dk=DK, dv=DV, B=1, H=2, N=100, d=128,
-             scale=0.125, causal=0, ws=WS):
+             scale=0.125, causal=0, cu=None, ws=WS):
     return lib.fa_bwd(*(ctypes.c_void_p(x) for x in (q, k, v, o, lse, do, dq, dk, dv)), B, H, N, d,
-                      ctypes.c_float(scale), causal, ctypes.c_void_p(ws), None)
+                      ctypes.c_float(scale), causal, None if cu is None else ctypes.c_void_p(cu),
+                      ctypes.c_void_p(ws), None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -216,13 +217,16 @@ def call_bwd(lib, q=Q, k=K, v=V, o=O, lse=L, do=DO, dq=DQ, dk=DK, dv=DV, B=1, H=
     (dict(N=0), SHAPE), (dict(H=(1 << 22) // 128 + 1), SHAPE), (dict(d=256), HEAD_DIM), (dict(d=32), HEAD_DIM),
     (dict(scale=0.0), SCALE), (dict(dq=DQ + 8), ALIGN), (dict(ws=WS + 4), ALIGN), (dict(lse=L + 2), ALIGN),
     (dict(dq=Q), ALIAS), (dict(dk=DO + 64), ALIAS), (dict(dv=DQ), ALIAS), (dict(ws=L), ALIAS),
-    (dict(ws=DK + 128), ALIAS),
+    (dict(ws=DK + 128), ALIAS), (dict(cu=0x80000002), ALIGN),
+    # packed (T = N = 100 tokens, H = 2): the workspace holds 2 * H * T floats
+    (dict(cu=0x80000000, B=4, ws=DK - 2 * 2 * 100 * 4 + 16), ALIAS),
 ])
 def test_bwd_invalid_arguments_are_rejected(lib, kw, code):
     assert call_bwd(lib, **kw) == code
 
 
 def test_bwd_workspace_size(lib):
-    assert fa.bwd_workspace_floats(2, 3, 100) == 2 * 3 * 4 * 64
+    # two floats (LSE * log2 e, delta) per LSE entry
+    assert fa.bwd_workspace_floats(2, 3, 100) == 2 * 2 * 3 * 100
     assert fa.bwd_workspace_floats(1, 1, 32) == 64
     assert fa.bwd_workspace_floats(0, 1, 32) == 0

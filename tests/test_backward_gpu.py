@@ -127,3 +127,80 @@ def test_bwd_full_size_sampled_heads(name):
                                   causal=run.causal)
         grads = [from_dev(g[b:b + 1, :, h:h + 1]) for g in (dq, dk, dv)]
         _check(grads, refs, f"{name} b={b} h={h}")
+
+
+# ---------------------------------------------------------------------------
+# Packed sequences (cu_seqlens): each sequence is its own attention problem.
+
+def _packed_inputs(lengths, d, causal, H=3, seed=81):
+    r = Run("packed_bwd", len(lengths), H, 0, d, causal, seed, varlen=True)
+    inp = make_inputs(r, lengths=lengths)
+    inp["do"] = make_grad(inp["q"].shape, seed + 5000)
+    return inp
+
+
+def _gpu_packed(inp):
+    q, k, v, do = (to_dev(inp[x]) for x in ("q", "k", "v", "do"))
+    cu = torch.from_numpy(np.asarray(inp["cu_seqlens"], dtype=np.int32)).to("cuda")
+    o, lse = fa.fwd(q, k, v, causal=inp["causal"], scale=inp["scale"], cu_seqlens=cu)
+    grads = fa.bwd(q, k, v, o, lse, do, causal=inp["causal"], scale=inp["scale"], cu_seqlens=cu)
+    torch.cuda.synchronize()
+    return grads
+
+
+def _oracle_packed(inp):
+    return attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale=inp["scale"],
+                              causal=inp["causal"], cu_seqlens=inp["cu_seqlens"])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_packed_small(d, causal):
+    """Empty, one-token and ragged sequences in one packed batch, every element."""
+    inp = _packed_inputs([1, 0, 5, 130, 257, 64, 300, 33], d, causal)
+    _check(_gpu_packed(inp), _oracle_packed(inp), f"packed d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_packed_many_sequences(causal):
+    """More than 64 sequences (the work decode walks them 64 at a time)."""
+    rng = np.random.default_rng(82)
+    lengths = [int(x) for x in rng.integers(0, 160, size=150)]
+    inp = _packed_inputs(lengths, 64, causal, H=2, seed=83)
+    _check(_gpu_packed(inp), _oracle_packed(inp), f"150 sequences causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_packed_equals_dense_bitwise(causal):
+    """Each packed sequence gives bitwise the gradients of a dense run of it alone."""
+    lengths = [37, 300, 129]
+    inp = _packed_inputs(lengths, 128, causal, H=2, seed=84)
+    packed = _gpu_packed(inp)
+    cu = inp["cu_seqlens"]
+    for b, n in enumerate(lengths):
+        t0 = int(cu[b])
+        one = {x: inp[x][None, t0:t0 + n] for x in ("q", "k", "v", "do")}
+        one.update(causal=causal, scale=inp["scale"])
+        dense = _gpu(one)
+        for g_packed, g_dense in zip(packed, dense):
+            assert torch.equal(g_packed[t0:t0 + n].view(torch.int16), g_dense[0].view(torch.int16))
+
+
+def test_bwd_packed_workload_sampled():
+    """The packed causal benchmark batch (32 sequences of 128..8192 tokens, 16
+    heads) at full size; the two shortest sequences are checked in full for
+    two heads each."""
+    run = RUNS["varlen_causal"]
+    inp = make_inputs(run)
+    inp["do"] = make_grad(inp["q"].shape, run.seed + 5000)
+    grads = _gpu_packed(inp)
+    cu = inp["cu_seqlens"]
+    lengths = np.diff(cu)
+    for b in np.argsort(lengths, kind="stable")[:2]:
+        t0, t1 = int(cu[b]), int(cu[b + 1])
+        for h in (0, run.H - 1):
+            sl = {x: inp[x][None, t0:t1, h:h + 1] for x in ("q", "k", "v", "do")}
+            refs = attention_backward(sl["q"], sl["k"], sl["v"], sl["do"], scale=inp["scale"],
+                                      causal=True)
+            got = [from_dev(g[t0:t1, h:h + 1])[None] for g in grads]
+            _check(got, refs, f"packed workload sequence {b} (n={t1 - t0}) h={h}")
