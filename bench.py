@@ -267,6 +267,28 @@ def masked_runs(torch, fa):
     return res
 
 
+def rescale_rates(torch, fa):
+    """How often the conditional rescale fires (counting instance of the
+    kernel, one launch per run and rule): the share of wave-steps (64 keys x 32
+    rows) whose O accumulator is rescaled, and of rows whose reference max moves,
+    over every key tile after each wave's first."""
+    from exact_attention_107_amd.workloads import RUNS, make_inputs
+    res = {}
+    for name in ("wide", "mid", "long_causal", "varlen_causal"):
+        log(f"[bench] rescale counts {name}")
+        ri = make_inputs(RUNS[name])
+        q, k, v = (to_dev(ri[x], torch) for x in ("q", "k", "v"))
+        cu = torch.from_numpy(ri["cu_seqlens"]).cuda() if ri["cu_seqlens"] is not None else None
+        res[name] = {}
+        for rule, mode in (("strict", fa.RESCALE_STRICT), ("threshold", fa.RESCALE_THRESHOLD)):
+            c = fa.rescale_counts(q, k, v, causal=ri["causal"], scale=ri["scale"], cu_seqlens=cu,
+                                  rescale_mode=mode)
+            res[name][rule] = {"step_rescale_rate": round(c["step_rescale_rate"], 5),
+                               "row_move_rate": round(c["row_move_rate"], 5), "steps": c["steps"]}
+        del q, k, v
+    return res
+
+
 def traffic_for(fingerprint: str):
     try:
         with open(TRAFFIC_FILE) as f:
@@ -408,6 +430,7 @@ def main() -> int:
                            for name in ("mid", "mid_causal", "bwd_long", "bwd_long_causal", "varlen_causal")}
         out["fp8"] = fp8_runs(torch, fa)
         out["masked"] = masked_runs(torch, fa)
+        out["rescale_rates"] = rescale_rates(torch, fa)
 
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")

@@ -60,9 +60,11 @@ int fa_tile_rows(int d) { return tile_rows_for(d); }
 
 int fa_tile_keys(int d) { return (d == 64 || d == 128 || d == 256) ? kTileKeys : 0; }
 
-int fa_fwd_variant(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
-                   int N, int d, float scale, int causal, const int32_t *cu_seqlens,
-                   hipStream_t stream, int exp_mode, int rescale_mode) {
+// Validation and launch of the forward; `counts` selects the counting
+// instance (d = 128, hardware exp2) and receives its statistics.
+static int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                    int N, int d, float scale, int causal, const int32_t *cu_seqlens,
+                    hipStream_t stream, int exp_mode, int rescale_mode, unsigned long long *counts) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULLPTR;
     if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
     if (d != 64 && d != 128 && d != 256) return FA_ERR_HEAD_DIM;
@@ -107,7 +109,9 @@ int fa_fwd_variant(const void *q, const void *k, const void *v, void *o, float *
     }
     if (grid <= 0 || grid > 0x7fffffffLL) return FA_ERR_SHAPE;
 
-    KernelFn fn = pick(d, causal != 0, varlen, exp_mode, rescale_mode);
+    prm.counts = counts;
+    KernelFn fn = counts ? select_count_d128(causal != 0, varlen, rescale_mode)
+                         : pick(d, causal != 0, varlen, exp_mode, rescale_mode);
     (void)hipGetLastError();  // clear a stale error so the check below is ours
     hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(grid)), dim3(waves_for(d) * 64), 0, stream, prm);
     if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
@@ -439,10 +443,37 @@ int fa_fwd_fp8(const void *q8, const void *k8, const void *vt8, const float *des
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_fwd_variant(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                   int N, int d, float scale, int causal, const int32_t *cu_seqlens,
+                   hipStream_t stream, int exp_mode, int rescale_mode) {
+    return fwd_impl(q, k, v, o, lse, B, H, N, d, scale, causal, cu_seqlens, stream, exp_mode, rescale_mode,
+                    nullptr);
+}
+
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
            int d, float scale, int causal, const int32_t *cu_seqlens, hipStream_t stream) {
     return fa_fwd_variant(q, k, v, o, lse, B, H, N, d, scale, causal, cu_seqlens, stream,
                           FA_EXP_HW, FA_RESCALE_THRESHOLD);
+}
+
+int fa_fwd_rescale_counts(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                          int N, int d, float scale, int causal, const int32_t *cu_seqlens,
+                          hipStream_t stream, int rescale_mode, unsigned long long *counts) {
+    if (!counts) return FA_ERR_NULLPTR;
+    if (misaligned(counts, 8)) return FA_ERR_ALIGN;
+    if (d != 128) return FA_ERR_HEAD_DIM;
+    if (rescale_mode != FA_RESCALE_STRICT && rescale_mode != FA_RESCALE_THRESHOLD) return FA_ERR_VARIANT;
+    const long long tokens = cu_seqlens ? static_cast<long long>(N) : static_cast<long long>(B) * N;
+    const long long elems = tokens * H * d;
+    if (B >= 1 && H >= 1 && N >= 1 && elems > 0 && elems <= (1LL << 46)) {
+        const size_t tb = static_cast<size_t>(elems) * 2, lb = static_cast<size_t>(tokens * H) * 4;
+        const void *bufs[] = {q, k, v, o};
+        for (const void *b : bufs)
+            if (b && overlap(counts, 32, b, tb)) return FA_ERR_ALIAS;
+        if (lse && overlap(counts, 32, lse, lb)) return FA_ERR_ALIAS;
+    }
+    return fwd_impl(q, k, v, o, lse, B, H, N, d, scale, causal, cu_seqlens, stream, FA_EXP_HW, rescale_mode,
+                    counts);
 }
 
 }  // extern "C"

@@ -23,6 +23,10 @@ struct Params {
     int wl, wr;          // key j visible to query i iff i - wl <= j <= i + wr (< 0: unbounded)
     const float *alibi;  // per-head slopes [H], or nullptr
     float inv_scale;     // 1 / scale
+    // rescale statistics (counting instances only): [0] wave-steps after the
+    // first tile, [1] of them with an O rescale, [2] rows whose reference max
+    // moved, [3] rows updated
+    unsigned long long *counts;
 };
 
 using KernelFn = void (*)(Params);
@@ -73,6 +77,8 @@ inline int waves_for(int d) {
 KernelFn select_d64(bool causal, bool varlen, int exp_mode, int rescale_mode);
 KernelFn select_d128(bool causal, bool varlen, int exp_mode, int rescale_mode);
 KernelFn select_d256(bool causal, bool varlen, int exp_mode, int rescale_mode);
+// Instance that also counts rescales (head dimension 128, hardware exp2).
+KernelFn select_count_d128(bool causal, bool varlen, int rescale_mode);
 // Window-mask / linear-bias instance (dense layout).
 KernelFn select_mods_d64();
 KernelFn select_mods_d128();

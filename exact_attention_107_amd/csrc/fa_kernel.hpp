@@ -359,7 +359,7 @@ __device__ __forceinline__ bool decode_work(const Params &p, Work &w) {
 // makes them visible.
 
 template <int D, int BC, int NW, int QB, bool CAUSAL, bool VARLEN, int EXPM, int RSM, bool SPLIT = false,
-          bool MODS = false>
+          bool MODS = false, bool COUNT = false>
 __global__ void __launch_bounds__(NW * 64)
 fa_fwd_kernel(Params p) {
     using SW = Swz<D>;
@@ -558,9 +558,11 @@ fa_fwd_kernel(Params p) {
             }
         }
     };
-    // Reference max update of every block from its tile's raw row max.
-    auto s_update = [&](float (&mx)[QB]) {
+    // Reference max update of every block from its tile's raw row max
+    // (`tally`: counted by the counting instances; not for the first tile).
+    auto s_update = [&](float (&mx)[QB], bool tally = true) {
         bool grow_any = false;
+        unsigned grown = 0;
 #pragma unroll
         for (int b = 0; b < QB; ++b) {
             const float x = xhalf_max(mx[b]);
@@ -579,6 +581,13 @@ fa_fwd_kernel(Params p) {
             l_run[b] *= alpha[b];
             m_run[b] = m_new;
             grow_any = grow_any || grow;
+            if constexpr (COUNT) grown += __popcll(__ballot(grow)) / 2;  // each row sits in two lanes
+        }
+        if constexpr (COUNT) {
+            if (tally && lane == 0) {
+                atomicAdd(&p.counts[2], static_cast<unsigned long long>(grown));
+                atomicAdd(&p.counts[3], static_cast<unsigned long long>(32 * QB));
+            }
         }
         if constexpr (RSM == FA_RESCALE_ALWAYS) {
             rescale_o = true;
@@ -778,7 +787,7 @@ fa_fwd_kernel(Params p) {
         if (need_mask(0)) s_mask(sa, 0);
         float mx[QB];
         s_rowmax(sa, mx);
-        s_update(mx);
+        s_update(mx, false);
     }
     __syncthreads();  // K tile 0 is reloaded at the start of iteration 0
 
@@ -796,9 +805,19 @@ fa_fwd_kernel(Params p) {
     // PAR = j & 1 selects the LDS tiles statically.  MASK: tile j+1 needs the
     // tail/causal mask (kept out of the hot loop so that nothing separates
     // phase [A] from phase [B]).
+    // counting instances: the O-rescale decision of step j (tile S_j), j >= 1
+    auto tally_step = [&](int j) {
+        if constexpr (COUNT) {
+            if (j > 0 && lane == 0) {
+                atomicAdd(&p.counts[0], 1ull);
+                if (rescale_o) atomicAdd(&p.counts[1], 1ull);
+            }
+        }
+    };
     auto full_step = [&](auto par, auto mask, f32x16 (&cur)[QB][NKB], f32x16 (&nxt)[QB][NKB], int j) {
         constexpr int PAR = decltype(par)::value;
         issue_loads(j, (PAR ? k_lds1 : k_lds0), (PAR ? v_lds0 : v_lds1));
+        tally_step(j);
         if (rescale_o) o_rescale();
         __builtin_amdgcn_sched_barrier(0);
         // the score MFMAs go first when the SIMD's two waves compete for
@@ -818,6 +837,7 @@ fa_fwd_kernel(Params p) {
     auto drain_step = [&](const f32x16 (&cur)[QB][NKB], int j) {
         const int par = j & 1;
         issue_loads(j, (par ? k_lds1 : k_lds0), (par ? v_lds0 : v_lds1));
+        tally_step(j);
         if (rescale_o) o_rescale();
         p_exp(cur);
         pv_mfma((par ? v_lds1 : v_lds0));
@@ -948,6 +968,22 @@ KernelFn select_exp(int expm, int rsm) {
         case FA_EXP_POLY: return select_rsm<D, CAUSAL, VARLEN, FA_EXP_POLY>(rsm);
         default: return select_rsm<D, CAUSAL, VARLEN, FA_EXP_MIXED>(rsm);
     }
+}
+
+template <int D>
+KernelFn select_count(bool causal, bool varlen, int rsm) {
+    constexpr int BC = kTileKeys, NW = Geometry<D>::kWaves, QB = Geometry<D>::kBlocks;
+    constexpr int HW = FA_EXP_HW, ST = FA_RESCALE_STRICT, TH = FA_RESCALE_THRESHOLD;
+    if (rsm == FA_RESCALE_STRICT) {
+        if (causal) return varlen ? fa_fwd_kernel<D, BC, NW, QB, true, true, HW, ST, false, false, true>
+                                  : fa_fwd_kernel<D, BC, NW, QB, true, false, HW, ST, false, false, true>;
+        return varlen ? fa_fwd_kernel<D, BC, NW, QB, false, true, HW, ST, false, false, true>
+                      : fa_fwd_kernel<D, BC, NW, QB, false, false, HW, ST, false, false, true>;
+    }
+    if (causal) return varlen ? fa_fwd_kernel<D, BC, NW, QB, true, true, HW, TH, false, false, true>
+                              : fa_fwd_kernel<D, BC, NW, QB, true, false, HW, TH, false, false, true>;
+    return varlen ? fa_fwd_kernel<D, BC, NW, QB, false, true, HW, TH, false, false, true>
+                  : fa_fwd_kernel<D, BC, NW, QB, false, false, HW, TH, false, false, true>;
 }
 
 template <int D>

@@ -11,4 +11,8 @@ KernelFn select_split_d128(bool causal) { return select_split<128>(causal); }
 
 KernelFn select_mods_d128() { return select_mods<128>(); }
 
+KernelFn select_count_d128(bool causal, bool varlen, int rescale_mode) {
+    return select_count<128>(causal, varlen, rescale_mode);
+}
+
 }  // namespace fa_detail

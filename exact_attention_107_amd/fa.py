@@ -22,7 +22,7 @@ RESCALE_ALWAYS, RESCALE_STRICT, RESCALE_THRESHOLD = 0, 1, 2
 EXPORTS = ("fa_fwd", "fa_fwd_variant", "fa_strerror", "fa_tile_rows", "fa_tile_keys",
            "fa_fwd_splitkv", "fa_merge", "fa_split_range", "fa_num_splits", "fa_bwd",
            "fa_bwd_workspace_floats", "fa_fwd_fp8", "fa_quantize_fp8", "fa_fp8_vt_stride",
-           "fa_fwd_masked")
+           "fa_fwd_masked", "fa_fwd_rescale_counts")
 
 _lib = None
 
@@ -75,6 +75,8 @@ def load(path: str | None = None):
     lib.fa_fp8_vt_stride.restype = i32
     lib.fa_fwd_masked.argtypes = [vp] * 5 + [i32, i32, i32, i32, ctypes.c_float, i32, i32, vp, vp]
     lib.fa_fwd_masked.restype = i32
+    lib.fa_fwd_rescale_counts.argtypes = common + [i32, vp]
+    lib.fa_fwd_rescale_counts.restype = i32
     if path is None:
         _lib = lib
     return lib
@@ -99,7 +101,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
         scale: float | None = None, cu_seqlens: torch.Tensor | None = None,
         exp_mode: int | None = None, rescale_mode: int | None = None,
         out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
-        stream: torch.cuda.Stream | None = None):
+        stream: torch.cuda.Stream | None = None, counts: torch.Tensor | None = None):
     """Exact attention forward on the GPU.
 
     q, k, v     bf16, ``[B, N, H, d]`` (dense) or ``[T, H, d]`` with
@@ -109,6 +111,10 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
                 one of the EXP_* / RESCALE_* constants (``fa_fwd_variant``).
     out, lse    optional preallocated outputs (``o`` like q; ``lse`` fp32
                 ``[B, H, N]`` or ``[H, T]``).
+    counts      optional int64 ``[4]`` device tensor: run the counting
+                instance (``fa_fwd_rescale_counts``, d = 128, hardware exp2,
+                ``rescale_mode`` strict or threshold), which adds its rescale
+                statistics to it.
     Returns ``(o, lse)``.  The kernel is queued on ``stream`` (default: the
     current stream); nothing is synchronised.
     """
@@ -152,8 +158,15 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
             int(B), int(H), int(N), int(d), ctypes.c_float(scale), int(bool(causal)),
             cu_ptr, ctypes.c_void_p(s.cuda_stream))
+    if counts is not None:
+        _check(counts, "counts", torch.int64, dev)
+        if counts.numel() != 4:
+            raise ValueError("counts must hold 4 int64 values")
     with torch.cuda.device(dev):
-        if exp_mode is None and rescale_mode is None:
+        if counts is not None:
+            rc = lib.fa_fwd_rescale_counts(*args, int(RESCALE_THRESHOLD if rescale_mode is None else rescale_mode),
+                                           counts.data_ptr())
+        elif exp_mode is None and rescale_mode is None:
             rc = lib.fa_fwd(*args)
         else:
             rc = lib.fa_fwd_variant(*args, int(EXP_HW if exp_mode is None else exp_mode),
@@ -161,6 +174,24 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
     if rc != 0:
         raise FaError(rc, strerror(rc))
     return out, lse
+
+
+def rescale_counts(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+                   scale: float | None = None, cu_seqlens: torch.Tensor | None = None,
+                   rescale_mode: int = RESCALE_THRESHOLD) -> dict:
+    """How often the conditional rescale fires (``fa_fwd_rescale_counts``).
+
+    Returns the four counters of the C ABI by name plus the two rates:
+    ``step_rescale_rate`` (wave-steps whose O accumulator was rescaled) and
+    ``row_move_rate`` (rows whose reference max moved), over every key tile
+    after each wave's first.
+    """
+    c = torch.zeros(4, dtype=torch.int64, device=q.device)
+    fwd(q, k, v, causal=causal, scale=scale, cu_seqlens=cu_seqlens, rescale_mode=rescale_mode, counts=c)
+    steps, rescaled, moved, rows = (int(x) for x in c.cpu().tolist())
+    return {"steps": steps, "rescaled_steps": rescaled, "rows_moved": moved, "rows": rows,
+            "step_rescale_rate": rescaled / steps if steps else 0.0,
+            "row_move_rate": moved / rows if rows else 0.0}
 
 
 def tile_rows(d: int) -> int:

@@ -230,6 +230,33 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o,
 long long fa_bwd_workspace_floats(int B, int H, int N);
 
 /*
+ * fa_fwd_rescale_counts: fa_fwd_variant (hardware exp2, d = 128 only) in an
+ * instance that also counts how often the conditional rescale of the online
+ * softmax ("FlashAttention 1-4 explained", FlashAttention-4 section: rescale
+ * only when the maximum grows; "Understanding FlashAttention V4", section 3.2:
+ * only when overflow is possible) actually rescales.  It writes O and LSE like
+ * fa_fwd_variant and ADDS to four device counters (the caller zeroes them):
+ *   counts[0]  wave-steps after each wave's first key tile (one per 64-key
+ *              tile and 32-row wave),
+ *   counts[1]  of those, steps whose O accumulator was rescaled (some row of
+ *              the wave moved its reference max),
+ *   counts[2]  rows whose reference max moved, over the same tiles,
+ *   counts[3]  rows updated (32 per counted wave-step).
+ * The atomics make it slower than fa_fwd: a measurement tool, not a variant.
+ *   rescale_mode  FA_RESCALE_STRICT or FA_RESCALE_THRESHOLD
+ *   counts        device array of 4 unsigned 64-bit integers, 8-byte aligned,
+ *                 not overlapping q, k, v, o or lse; borrowed.
+ * Returns fa_fwd_variant's codes, FA_ERR_NULLPTR for counts == NULL,
+ * FA_ERR_ALIGN, FA_ERR_HEAD_DIM for d != 128, FA_ERR_VARIANT for another
+ * rescale_mode, FA_ERR_ALIAS for overlapping counters.
+ */
+int fa_fwd_rescale_counts(const void *q, const void *k, const void *v, void *o,
+                          float *lse, int B, int H, int N, int d, float scale,
+                          int causal, const int32_t *cu_seqlens,
+                          hipStream_t stream, int rescale_mode,
+                          unsigned long long *counts);
+
+/*
  * fa_fwd_masked: fa_fwd with a window mask and an optional linear distance
  * bias (dense layout) -- built-in forms of the score modifications and masks
  * that FlexAttention user code expresses (FlashAttention-4 as a FlexAttention

@@ -230,3 +230,25 @@ def test_bwd_workspace_size(lib):
     assert fa.bwd_workspace_floats(2, 3, 100) == 2 * 2 * 3 * 100
     assert fa.bwd_workspace_floats(1, 1, 32) == 64
     assert fa.bwd_workspace_floats(0, 1, 32) == 0
+
+
+def call_counts(lib, counts=0x700000, d=128, rescale_mode=2, **kw):
+    args = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, N=64, scale=0.125, causal=0, cu=None)
+    args.update(kw)
+    return lib.fa_fwd_rescale_counts(
+        ctypes.c_void_p(args["q"]), ctypes.c_void_p(args["k"]), ctypes.c_void_p(args["v"]),
+        ctypes.c_void_p(args["o"]), ctypes.c_void_p(args["lse"]), args["B"], args["H"], args["N"], d,
+        ctypes.c_float(args["scale"]), args["causal"],
+        ctypes.c_void_p(args["cu"]) if args["cu"] else None, None, rescale_mode,
+        ctypes.c_void_p(counts) if counts else None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(counts=0), NULLPTR), (dict(counts=0x700004), ALIGN), (dict(d=64), HEAD_DIM),
+    (dict(d=256), HEAD_DIM), (dict(rescale_mode=0), VARIANT), (dict(rescale_mode=3), VARIANT),
+    (dict(counts=Q + 64), ALIAS), (dict(counts=L), ALIAS),
+    (dict(q=0), NULLPTR), (dict(N=0), SHAPE), (dict(scale=float("nan")), SCALE),
+    (dict(o=Q), ALIAS),
+])
+def test_rescale_counts_invalid_arguments_are_rejected(lib, kw, code):
+    assert call_counts(lib, **kw) == code
