@@ -67,8 +67,10 @@ def time_launches(launch, steps: int, warmup: int, torch):
     return wall * 1e3 / steps, float(np.mean(per)), float(np.median(per)), float(np.min(per))
 
 
-def cpu_baseline(inp, target_s: float):
-    """The oracle on a bounded row sample of the same workload, all host cores."""
+def cpu_baseline(inp, target_s: float, gpu_out=None):
+    """The oracle on a bounded row sample of the same workload, all host cores.
+    With ``gpu_out = (o, lse, torch)`` (the timed launch's outputs) the same
+    rows are also compared with the GPU result."""
     import oracle
     from exact_attention_107_amd.workloads import flops
     threads = oracle.default_threads()
@@ -97,17 +99,41 @@ def cpu_baseline(inp, target_s: float):
     count = int(min(max(len(calib) * target_s / max(dt, 1e-3), len(calib)), 2_000_000))
     rows = rows_of(count)
     t0 = time.perf_counter()
-    oracle.attention(inp["q"], inp["k"], inp["v"], scale=inp["scale"], causal=inp["causal"],
-                     cu_seqlens=inp["cu_seqlens"], rows=rows, nthreads=threads)
+    o_ref, lse_ref = oracle.attention(inp["q"], inp["k"], inp["v"], scale=inp["scale"], causal=inp["causal"],
+                                      cu_seqlens=inp["cu_seqlens"], rows=rows, nthreads=threads)
     dt = time.perf_counter() - t0
     f = credited(rows)
     total = flops(lengths, H, inp["d"], inp["causal"])
+    parity = None
+    if gpu_out is not None:
+        parity = sampled_parity(inp, rows, o_ref, lse_ref, *gpu_out)
     return {
         "value": f / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
         "sample": f"{count} random query rows of the {inp['name']} run "
                   f"({f / total * 100:.3f}% of its credited flops), fp64, {dt:.1f} s wall",
         "seconds": dt, "full_run_seconds_extrapolated": dt * total / f,
-    }
+    }, parity
+
+
+def sampled_parity(inp, rows, o_ref, lse_ref, o, lse, torch):
+    """The timed launch's O and LSE on the oracle's sample rows, with the
+    forward's tolerances (bf16 O: max 2e-2, mean 2e-3; fp32 LSE: max 1e-3)."""
+    from exact_attention_107_amd.workloads import bf16_to_f32
+    r = torch.from_numpy(rows).cuda()
+    b, h, i = r[:, 0], r[:, 1], r[:, 2]
+    if inp["cu_seqlens"] is None:
+        og, lg = o[b, i, h], lse[b, h, i]
+    else:
+        tok = torch.from_numpy(inp["cu_seqlens"].astype(np.int64)).cuda()[b] + i
+        og, lg = o[tok, h], lse[h, tok]
+    og = bf16_to_f32(og.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    lg = lg.cpu().numpy().astype(np.float64)
+    do, dl = np.abs(og - o_ref), np.abs(lg - lse_ref)
+    res = {"kind": "oracle rows of the CPU baseline sample", "rows": int(len(rows)),
+           "max_abs_o": float(do.max()), "mean_abs_o": float(do.mean()), "max_abs_lse": float(dl.max()),
+           "tol": {"max_abs_o": 2e-2, "mean_abs_o": 2e-3, "max_abs_lse": 1e-3}}
+    res["pass"] = bool(res["max_abs_o"] <= 2e-2 and res["mean_abs_o"] <= 2e-3 and res["max_abs_lse"] <= 1e-3)
+    return res
 
 
 def split_kv_runs(torch, fa):
@@ -433,8 +459,10 @@ def main() -> int:
         out["rescale_rates"] = rescale_rates(torch, fa)
 
     if not args.no_cpu_baseline:
+        launch()  # the variants above reused o and lse: restore the timed launch's outputs
+        torch.cuda.synchronize()
         log("[bench] CPU oracle baseline")
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        out["cpu_baseline"], out["parity"] = cpu_baseline(inp, args.cpu_seconds, (o, lse, torch))
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -453,7 +453,7 @@ int fa_fwd_variant(const void *q, const void *k, const void *v, void *o, float *
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
            int d, float scale, int causal, const int32_t *cu_seqlens, hipStream_t stream) {
     return fa_fwd_variant(q, k, v, o, lse, B, H, N, d, scale, causal, cu_seqlens, stream,
-                          FA_EXP_HW, FA_RESCALE_THRESHOLD);
+                          FA_EXP_HW, FA_RESCALE_STRICT);
 }
 
 int fa_fwd_rescale_counts(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,

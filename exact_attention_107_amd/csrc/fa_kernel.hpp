@@ -517,11 +517,19 @@ fa_fwd_kernel(Params p) {
     for (int b = 0; b < QB; ++b)
 #pragma unroll
         for (int i = 0; i < NDB; ++i) oacc[b][i] = f32x16{};
-    float m_run[QB], l_run[QB], m_use[QB], alpha[QB];
+    // Threshold rescale: the reference max may trail a row's true max by up to
+    // 8, so a row dominated by one key gives that key a weight up to 2^8, which
+    // bf16 rounds by up to 2^-9; dividing O by the sum of the bf16 weights the
+    // P V product actually uses keeps O a weighted mean of V rows (the LSE
+    // keeps the fp32 sum).  Under the strict and always rules the dominant
+    // weight is exactly 1 and O is divided by the fp32 sum.
+    constexpr bool kBf16Norm = RSM == FA_RESCALE_THRESHOLD;
+    float m_run[QB], l_run[QB], lb_run[QB], m_use[QB], alpha[QB];
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
         m_run[b] = -INFINITY;  // reference max, scaled log2 units
-        l_run[b] = 0.0f;       // this lane's partial row sum
+        l_run[b] = 0.0f;       // this lane's partial row sum (fp32 weights: the LSE)
+        lb_run[b] = 0.0f;      // the same over the bf16 weights P V uses (divides O)
         m_use[b] = 0.0f;       // subtrahend of the tile being exponentiated
         alpha[b] = 1.0f;       // pending rescale of O for that tile
     }
@@ -579,6 +587,7 @@ fa_fwd_kernel(Params p) {
             m_use[b] = (m_new == -INFINITY) ? 0.0f : m_new;
             alpha[b] = __builtin_amdgcn_exp2f(m_run[b] - m_use[b]);  // 1 if unchanged, 0 from -inf
             l_run[b] *= alpha[b];
+            if constexpr (kBf16Norm) lb_run[b] *= alpha[b];
             m_run[b] = m_new;
             grow_any = grow_any || grow;
             if constexpr (COUNT) grown += __popcll(__ballot(grow)) / 2;  // each row sits in two lanes
@@ -626,12 +635,16 @@ fa_fwd_kernel(Params p) {
     auto p_elem = [&](const f32x16 (&s)[QB][NKB], int b, int e) {
         pe[b][e] = exp2_sel<EXPM>(__builtin_fmaf(s[b][e >> 4][e & 15], cs, -m_use[b]), e);
     };
+    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
     auto p_pack = [&](int b, int t, float &rsum) {
         uint32_t pk[4];
 #pragma unroll
         for (int i = 0; i < 8; i += 2) {
             rsum += pe[b][8 * t + i] + pe[b][8 * t + i + 1];
             pk[i >> 1] = pack_bf16x2(pe[b][8 * t + i], pe[b][8 * t + i + 1]);
+            if constexpr (kBf16Norm)
+                lb_run[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[i >> 1]), ones,
+                                                            lb_run[b], false);
         }
         u32x4 pv = {pk[0], pk[1], pk[2], pk[3]};
         pf[b][t] = __builtin_bit_cast(bf16x8, pv);
@@ -899,8 +912,9 @@ fa_fwd_kernel(Params p) {
     for (int b = 0; b < QB; ++b) {
         const int rowb = wrow0 + 32 * b;
         const float l = xhalf_sum(l_run[b]);
+        const float lb = kBf16Norm ? xhalf_sum(lb_run[b]) : l;
         // rows >= n fall outside the buffer and are dropped
-        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+        const float inv = lb > 0.0f ? 1.0f / lb : 0.0f;
         if constexpr (SPLIT) {
             // normalised fp32 partial O of this key range, and its LSE
             const long long sbase = static_cast<long long>(w.split) * p.B * p.N * p.H * D + base;

@@ -164,13 +164,13 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
             raise ValueError("counts must hold 4 int64 values")
     with torch.cuda.device(dev):
         if counts is not None:
-            rc = lib.fa_fwd_rescale_counts(*args, int(RESCALE_THRESHOLD if rescale_mode is None else rescale_mode),
+            rc = lib.fa_fwd_rescale_counts(*args, int(RESCALE_STRICT if rescale_mode is None else rescale_mode),
                                            counts.data_ptr())
         elif exp_mode is None and rescale_mode is None:
             rc = lib.fa_fwd(*args)
         else:
             rc = lib.fa_fwd_variant(*args, int(EXP_HW if exp_mode is None else exp_mode),
-                                    int(RESCALE_THRESHOLD if rescale_mode is None else rescale_mode))
+                                    int(RESCALE_STRICT if rescale_mode is None else rescale_mode))
     if rc != 0:
         raise FaError(rc, strerror(rc))
     return out, lse
@@ -178,7 +178,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
 
 def rescale_counts(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
                    scale: float | None = None, cu_seqlens: torch.Tensor | None = None,
-                   rescale_mode: int = RESCALE_THRESHOLD) -> dict:
+                   rescale_mode: int = RESCALE_STRICT) -> dict:
     """How often the conditional rescale fires (``fa_fwd_rescale_counts``).
 
     Returns the four counters of the C ABI by name plus the two rates:

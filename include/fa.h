@@ -107,10 +107,12 @@ enum fa_rescale_mode {
  *   cu_seqlens NULL (dense) or a device int32 array of B+1 non-decreasing
  *             offsets with cu_seqlens[0] = 0 and cu_seqlens[B] = N.
  *   stream    HIP stream the kernel is queued on (NULL: default stream).
- * Returns FA_OK or an fa_status code.  Uses the library's default variant
- * (hardware exp, threshold conditional rescale: the fastest variant measured
- * on every shape tried; strict and threshold give the same O and LSE up to
- * rounding).
+ * Returns FA_OK or an fa_status code.  Uses the library's default variant:
+ * hardware exp2 and the strict conditional rescale (O and l are rescaled only
+ * when some row's maximum grows; the largest weight of a row is then exactly 1
+ * in bf16).  The threshold rule is faster on unit-variance inputs but lets a
+ * dominant weight reach 2^8, which bf16 cannot hold exactly, so its instances
+ * divide O by the sum of the bf16 weights at some cost (see fa_fwd_variant).
  */
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
            int B, int H, int N, int d, float scale, int causal,
@@ -119,7 +121,11 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
 /*
  * fa_fwd_variant: fa_fwd with an explicit exp evaluation (fa_exp_mode) and
  * rescale policy (fa_rescale_mode).  Every variant computes the same O and
- * LSE up to rounding; they differ only in speed.
+ * LSE up to rounding, within the forward's tolerances; they differ in speed.
+ * Threshold instances divide O by the sum of the bf16-rounded weights that
+ * the P V product uses (its reference max may trail a row's maximum by up to
+ * 8, so a dominant weight is not exact in bf16); the LSE always uses the fp32
+ * sum.
  */
 int fa_fwd_variant(const void *q, const void *k, const void *v, void *o,
                    float *lse, int B, int H, int N, int d, float scale,
