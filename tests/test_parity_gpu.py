@@ -142,11 +142,12 @@ FULL_RUNS = ["mid", "mid_causal", "long_causal", "varlen_causal", "wide", "wide_
 
 @pytest.mark.parametrize("name", FULL_RUNS)
 def test_full_size_run(name):
-    """The full-size runs: sampled rows vs the oracle, whole output finite."""
+    """The full-size runs: 12 000 sampled rows (tile boundaries, sequence ends,
+    random rows) vs the oracle, whole output finite."""
     inp = make_inputs(RUNS[name])
     o, lse = run_gpu(inp)
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
-    m = sampled_parity(inp, o, lse)
+    m = sampled_parity(inp, o, lse, count=12000)
     print(name, m)
     assert_within(m, name)
 
