@@ -315,6 +315,24 @@ def rescale_rates(torch, fa):
     return res
 
 
+def device_clock(arch: str):
+    """Max engine clock and CU count that rocminfo reports for the GPU agent."""
+    import re
+    import subprocess
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    name = arch.split(":")[0]
+    for block in txt.split("Agent ")[1:]:
+        if re.search(r"Name:\s+" + re.escape(name) + r"\s", block):
+            clk = re.search(r"Max Clock Freq\. \(MHz\):\s+(\d+)", block)
+            cus = re.search(r"Compute Unit:\s+(\d+)", block)
+            return {"max_sclk_mhz": int(clk.group(1)) if clk else None,
+                    "compute_units": int(cus.group(1)) if cus else None}
+    return None
+
+
 def traffic_for(fingerprint: str):
     try:
         with open(TRAFFIC_FILE) as f:
@@ -415,7 +433,9 @@ def main() -> int:
             "per_launch": "4*B*H*N^2*d flops (halved if causal) / mean HIP-event duration",
         },
         "device": {"name": props.name, "cus": props.multi_processor_count,
-                   "arch": getattr(props, "gcnArchName", "")},
+                   "arch": getattr(props, "gcnArchName", ""),
+                   "rocminfo": device_clock(getattr(props, "gcnArchName", "gfx950")),
+                   "peak_formula": "256 CU x 2.4 GHz x 4096 dense BF16 flop/clk/CU (spec)"},
         "kernel_fingerprint": fp,
     }
 
