@@ -162,6 +162,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
         _check(counts, "counts", torch.int64, dev)
         if counts.numel() != 4:
             raise ValueError("counts must hold 4 int64 values")
+        if exp_mode not in (None, EXP_HW):
+            raise ValueError("the counting instance evaluates exp2 in hardware (exp_mode EXP_HW)")
     with torch.cuda.device(dev):
         if counts is not None:
             rc = lib.fa_fwd_rescale_counts(*args, int(RESCALE_STRICT if rescale_mode is None else rescale_mode),
