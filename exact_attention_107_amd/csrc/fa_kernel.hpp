@@ -21,21 +21,23 @@
 //    ds_read_b64_tr_b16, so P never leaves the VGPRs.  The O^T accumulator
 //    again gives each lane one query row, so the rescale by exp(m_old - m_new)
 //    is a per-lane scalar multiply.
-//  * K and V tiles are staged global -> VGPR -> LDS, double-buffered: the
-//    global loads of tile j+1 are in flight while tile j is computed.  The
-//    LDS rows are padded so that both the K reads (8 lanes, 8 rows, one
-//    16-byte chunk) and the transposing V reads (16 lanes, 4 rows, 32 bytes)
-//    touch distinct banks.
+//  * K and V tiles go from global memory straight into LDS (buffer loads with
+//    the LDS destination), two K and two V tiles: K_{j+2} and V_{j+1} stream
+//    in while tile j is computed.  The 16-byte chunks of each LDS row are
+//    XOR-permuted so that the K reads (16 consecutive rows, one chunk) and
+//    the transposing V reads (4 rows x 4 chunks) touch distinct banks.
 //  * exp is evaluated as exp2 of (s * scale * log2 e - m) with the hardware
 //    v_exp_f32, or with a degree-3 polynomial on the FMA units (section 3.2
 //    of the FlashAttention V4 explainer), or half and half.
 //  * Conditional rescale (FlashAttention-4 section of the 1-4 post): a wave
-//    skips the O multiply when no row max grew, or, in threshold mode, keeps
-//    its reference max until a row max exceeds it by more than 8.
+//    skips the O multiply when no row max grew (strict, the default), or, in
+//    threshold mode, keeps its reference max until a row max exceeds it by
+//    more than 8 and then divides O by the sum of the bf16 weights it used.
 //  * Causal tiles that are fully masked are never visited (FlashAttention-2
-//    engineering notes); the tile order puts the longest tiles first and keeps
-//    the work items of one (sequence, head) on one XCD so that its K/V stream
-//    is shared through that XCD's L2.
+//    engineering notes); causal work is ordered longest first, non-causal
+//    work gives each XCD a contiguous run of items (the query tiles of one
+//    head, whose K/V stream its L2 then serves), and packed sequences go
+//    longest first with the heads of one query tile together.
 //
 // Every function of the library's C ABI is declared in include/fa.h.
 
