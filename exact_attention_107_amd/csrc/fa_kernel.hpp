@@ -552,6 +552,21 @@ fa_fwd_kernel(Params p) {
 #pragma unroll
         for (int b = 0; b < QB; ++b) {
             const int qrow = wrow0 + 32 * b + c;
+            if constexpr (!MODS) {
+                // key = kv0 + 4 hh + C with C = 32 kb2 + 8 (r >> 2) + (r & 3) fixed per
+                // element: the key is visible iff C < lim, one compare with an inline
+                // constant per element (measured +3 % on short causal runs)
+                int lim = n - kv0 - 4 * hh;
+                if (CAUSAL) lim = min(lim, qrow - kv0 - 4 * hh + 1);
+#pragma unroll
+                for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int C = kb2 * 32 + (r >> 2) * 8 + (r & 3);
+                        s[b][kb2][r] = C < lim ? s[b][kb2][r] : -INFINITY;
+                    }
+                continue;
+            }
 #pragma unroll
             for (int kb2 = 0; kb2 < NKB; ++kb2) {
 #pragma unroll
