@@ -172,10 +172,18 @@ __device__ __forceinline__ void lgkm_wait(bf16x8 &v) {
 }
 
 // Max of x over lanes l and l ^ 32.
+// max of two floats that are never signalling NaNs: a plain v_max_f32, without
+// the quieting of the inputs that fmaxf implies
+__device__ __forceinline__ float vmax(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 __device__ __forceinline__ float xhalf_max(float x) {
     const uint32_t u = __float_as_uint(x);
     auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    return vmax(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 
 __device__ __forceinline__ float xhalf_sum(float x) {
@@ -591,17 +599,21 @@ fa_fwd_kernel(Params p) {
 #pragma unroll
         for (int b = 0; b < QB; ++b) {
             const float x = xhalf_max(mx[b]);
-            const float mt = (x == -INFINITY) ? -INFINITY : x * cs;
+            const float mt = x * cs;  // cs > 0: -inf stays -inf
             float m_new;
             bool grow;
             if constexpr (RSM == FA_RESCALE_THRESHOLD) {
                 grow = mt > m_run[b] + kTau;  // also true for the first finite tile
                 m_new = grow ? mt : m_run[b];
             } else {
-                m_new = fmaxf(m_run[b], mt);
+                m_new = vmax(m_run[b], mt);
                 grow = m_new > m_run[b];
             }
-            m_use[b] = (m_new == -INFINITY) ? 0.0f : m_new;
+            // a row with no visible key so far keeps m = -inf; its subtrahend is then a
+            // large finite value, so that -inf - m_use is -inf and never NaN
+            float mu;
+            asm("v_max_f32 %0, 0xf149f2ca, %1" : "=v"(mu) : "v"(m_new));  // max(m_new, -1e30)
+            m_use[b] = mu;
             alpha[b] = __builtin_amdgcn_exp2f(m_run[b] - m_use[b]);  // 1 if unchanged, 0 from -inf
             l_run[b] *= alpha[b];
             if constexpr (kBf16Norm) lb_run[b] *= alpha[b];
