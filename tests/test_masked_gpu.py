@@ -62,7 +62,7 @@ def test_masked_full_size_sampled():
     o, lse = _run(inp, 1024, 0, slopes)
     rng = np.random.Generator(np.random.PCG64(3))
     rows = np.array([(0, int(rng.integers(16)), i) for i in
-                     [0, 1, 1023, 1024, 1025, 8191, 16383] + list(rng.integers(0, 16384, 120))], dtype=np.int64)
+                     [0, 1, 1023, 1024, 1025, 8191, 16383] + list(rng.integers(0, 16384, 1200))], dtype=np.int64)
     ro, rl = omods.attention(inp["q"], inp["k"], inp["v"], scale=inp["scale"], left=1024, right=0, slopes=slopes,
                              rows=rows)
     rt = torch.from_numpy(rows)

@@ -170,7 +170,7 @@ def test_splitkv_full_size_sampled(name):
     assert S > 1
     o, lse = fa.fwd_splitkv(q, k, v, causal=run.causal, scale=inp["scale"], splits=S)
     torch.cuda.synchronize()
-    m = sampled_parity(inp, o, lse, count=256, seed=5)
+    m = sampled_parity(inp, o, lse, count=6000, seed=5)
     print(name, "S =", S, m)
     assert_within(m, name)
     # every row's LSE is finite and O is finite
