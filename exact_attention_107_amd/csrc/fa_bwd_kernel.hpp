@@ -79,12 +79,16 @@ template <int D, int ROWS, int NW> struct BwdDma {
         const int r = pos / RB, pc = (pos % RB) / 16;
         return r * rs_bytes + ((pc ^ BwdTile<D>::sg(r)) << 4);
     }
-    static __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, char *tile, int wave, int voff,
-                                                int rs_bytes) {
+    // Rows row0 .. row0 + ROWS - 1 of the tensor at g (row stride rs
+    // elements); rows at or past n read as zeros.  Load i covers rows
+    // NW i RPB .. further on than the lane offset says, so it gets a resource
+    // based at those rows: the size check covers the lane offset only.
+    static __device__ __forceinline__ void load(const uint16_t *g, long long rs, int row0, int n, char *tile,
+                                                int wave, int voff) {
 #pragma unroll
         for (int i = 0; i < PER; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, tile + (wave + NW * i) * 1024), 16, voff,
-                                                     NW * i * RPB * rs_bytes, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(g, rs, row0 + NW * i * RPB, n),
+                                                     LDS_PTR(void, tile + (wave + NW * i) * 1024), 16, voff, 0, 0, 0);
     }
 };
 
@@ -332,20 +336,15 @@ fa_bwd_dkdv_kernel(BwdParams p) {
     const int nqb = (n + BQ - 1) / BQ;
     auto dma_block = [&](int qb, char *qd, char *dd, float *sd) __attribute__((always_inline)) {
         const int q0 = qb * BQ;
-        const auto qrs = make_rsrc(p.q + base + q0 * rs, (long long)(n - q0) * rs_bytes);
-        QDMA::load(qrs, qd, wave, qvoff, rs_bytes);
-        const auto drs = make_rsrc(p.dout + base + q0 * rs, (long long)(n - q0) * rs_bytes);
-        QDMA::load(drs, dd, wave, qvoff, rs_bytes);
+        QDMA::load(p.q + base, rs, q0, n, qd, wave, qvoff);
+        QDMA::load(p.dout + base, rs, q0, n, dd, wave, qvoff);
         if (wave == 0) {
             // rows past the sequence read (0, 0); the mask gives them P = 0
             const auto srs = make_rsrc(stats_seq + 2 * q0, (long long)(n - q0) * 8);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, LDS_PTR(void, sd), 4, st_off, 0, 0, 0);
         }
     };
-    {
-        const auto vrs = make_rsrc(p.v + base + j0 * rs, (long long)(n - j0) * rs_bytes);
-        VDMA::load(vrs, v_lds, wave, vvoff, rs_bytes);
-    }
+    VDMA::load(p.v + base, rs, j0, n, v_lds, wave, vvoff);
     if (qb0 < nqb) dma_block(qb0, q_lds0, do_lds0, st_lds0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -566,10 +565,8 @@ fa_bwd_dq_kernel(BwdParams p) {
 
     auto dma_tile = [&](int j, char *kd, char *vd) __attribute__((always_inline)) {
         const int kv0 = j * BC;
-        const auto krs = make_rsrc(p.k + base + kv0 * rs, (long long)(n - kv0) * rs_bytes);
-        KDMA::load(krs, kd, wave, kvoff, rs_bytes);
-        const auto vrs = make_rsrc(p.v + base + kv0 * rs, (long long)(n - kv0) * rs_bytes);
-        KDMA::load(vrs, vd, wave, kvoff, rs_bytes);
+        KDMA::load(p.k + base, rs, kv0, n, kd, wave, kvoff);
+        KDMA::load(p.v + base, rs, kv0, n, vd, wave, kvoff);
     };
     dma_tile(0, k_lds0, v_lds0);
     __builtin_amdgcn_s_waitcnt(0);

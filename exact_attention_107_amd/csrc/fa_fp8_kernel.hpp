@@ -234,16 +234,21 @@ fa_fp8_fwd_kernel(Fp8Params p) {
     f32x16 sa[2], sb[2];
     auto dma_k = [&](int j, char *kd) __attribute__((always_inline)) {
         const int kv0 = j * BC;
-        const auto krs = make_rsrc(p.k + base8 + static_cast<long long>(kv0) * rs, (long long)(n - kv0) * rs);
+        // load i starts NW i (1024 / KRB) rows past the lane offset's row: its
+        // resource is based there (the size check covers the lane offset only)
 #pragma unroll
-        for (int i = 0; i < KBLK / NW; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, LDS_PTR(void, kd + (wave + NW * i) * 1024), 16, kvo,
-                                                     NW * i * (1024 / KRB) * rs, 0, 0);
+        for (int i = 0; i < KBLK / NW; ++i) {
+            const int r0 = kv0 + NW * i * (1024 / KRB);
+            const auto krs = make_rsrc(p.k + base8 + static_cast<long long>(r0) * rs, (long long)(n - r0) * rs);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, LDS_PTR(void, kd + (wave + NW * i) * 1024), 16, kvo, 0, 0,
+                                                     0);
+        }
     };
     auto dma_v = [&](int j, char *vd) __attribute__((always_inline)) {
         const int kv0 = j * BC;
         // V^T rows are np bytes apart, so a 64-key tile never crosses a row;
-        // keys past n hold the zero padding
+        // keys past n hold the zero padding.  The scalar offset (d rows) stays
+        // inside the head's D x np bytes, which the resource spans.
         const auto vrs = make_rsrc(vt + kv0, (long long)D * np - kv0);
 #pragma unroll
         for (int i = 0; i < VBLK / NW; ++i)

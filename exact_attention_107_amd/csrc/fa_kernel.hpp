@@ -134,11 +134,23 @@ template <int D> struct Swz {
 
 // Raw buffer resource over `bytes` bytes at `base` (gfx9 word 3); loads past
 // the end return zeros (also into LDS) and stores past the end are dropped.
+// The hardware checks only the per-lane offset (plus the immediate) against
+// the size, never the scalar offset: a row offset must therefore go into the
+// base and size of the resource (rows_rsrc), and the scalar offset may only
+// hold a column offset that stays inside a row the lane offset has
+// already bounded.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, long long bytes) {
     const long long lim = bytes < 0 ? 0 : (bytes > 0xffffffffLL ? 0xffffffffLL : bytes);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
                                              static_cast<int>(static_cast<uint32_t>(lim)),
                                              0x00020000);
+}
+
+// Resource over rows row0 .. n-1 of a row-strided tensor (`row_bytes` apart,
+// element pointer `base` at row 0): rows at or past n read as zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t *base, long long row_elems,
+                                                            int row0, int n) {
+    return make_rsrc(base + row0 * row_elems, (long long)(n - row0) * row_elems * 2);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -413,14 +425,14 @@ fa_fwd_kernel(Params p) {
     // Q[wrow0 + 32 b + c][kk*16 + hh*8 .. +8]; rows >= n read as zeros.
     bf16x8 qf[QB][KK];
     {
-        const auto qrs = make_rsrc(qg + wrow0 * rs, (long long)(n - wrow0) * rs * 2);
         const int voff = (c * static_cast<int>(rs) + hh * 8) * 2;
 #pragma unroll
-        for (int b = 0; b < QB; ++b)
+        for (int b = 0; b < QB; ++b) {
+            const auto qrs = rows_rsrc(qg, rs, wrow0 + 32 * b, n);
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
-                qf[b][kk] = __builtin_bit_cast(
-                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, voff + kk * 32, 32 * b * static_cast<int>(rs) * 2, 0));
+                qf[b][kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, voff + kk * 32, 0, 0));
+        }
     }
 
     // keys past kv_end are invisible to every row of the workgroup: the causal
@@ -468,25 +480,26 @@ fa_fwd_kernel(Params p) {
         const int r = pos / RB, pc = (pos % RB) / 16;
         voff = r * rs_bytes + ((pc ^ Swz<D>::fv(r)) << 4);
     }
+    // A load whose rows start past the wave's first rows gets a resource
+    // based at those rows (the size check covers the lane offset only); the
+    // scalar offset carries just the plane's column offset.
     auto dma_k = [&](char *tile, int j) {
         const int kv0 = (kt0 + j) * BC;
-        const auto rsrc = make_rsrc(kg + kv0 * rs, (long long)(n - kv0) * rs_bytes);
 #pragma unroll
         for (int i = 0; i < KPW; ++i) {
             const int I = wave + NW * i;              // load index within the tile
             const int di = (I % 8) - (wave % 8);      // rows of this load past the wave's first / 8
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, tile + I * 1024), 16, koff,
-                                                     8 * di * rs_bytes + (I / 8) * 128, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(kg, rs, kv0 + 8 * di, n),
+                                                     LDS_PTR(void, tile + I * 1024), 16, koff, (I / 8) * 128, 0, 0);
         }
     };
     constexpr int VROWS = 1024 / RB;     // V rows per 1 KB block
     auto dma_v = [&](char *tile, int j) {
         const int kv0 = (kt0 + j) * BC;
-        const auto rsrc = make_rsrc(vg + kv0 * rs, (long long)(n - kv0) * rs_bytes);
 #pragma unroll
         for (int i = 0; i < BPW; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, tile + (wave + NW * i) * 1024), 16,
-                                                     voff, NW * i * VROWS * rs_bytes, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(vg, rs, kv0 + NW * i * VROWS, n),
+                                                     LDS_PTR(void, tile + (wave + NW * i) * 1024), 16, voff, 0, 0, 0);
     };
 
     // ---- LDS fragment reads --------------------------------------------------------
