@@ -36,6 +36,10 @@ bool token_stride_ok(int H, int d) { return static_cast<long long>(H) * d <= (1L
 
 int key_tiles(int N) { return (N + kTileKeys - 1) / kTileKeys; }
 
+// Longest sequence of the window-mask forward: row + window edge (each below
+// N after clamping) plus a tile must fit in an int.
+constexpr int kMaskedMaxN = 1 << 30;
+
 }  // namespace
 
 extern "C" {
@@ -334,7 +338,8 @@ int fa_fwd_masked(const void *q, const void *k, const void *v, void *o, float *l
         return FA_ERR_ALIGN;
     const long long rows = static_cast<long long>(B) * N * H;
     const long long elems = rows * d;
-    if (elems <= 0 || elems > (1LL << 46) || !token_stride_ok(H, d)) return FA_ERR_SHAPE;
+    // window edges are added to row and key indices in 32-bit arithmetic
+    if (elems <= 0 || elems > (1LL << 46) || !token_stride_ok(H, d) || N > kMaskedMaxN) return FA_ERR_SHAPE;
     const size_t tb = static_cast<size_t>(elems) * 2, lb = static_cast<size_t>(rows) * 4;
     const size_t sb = static_cast<size_t>(H) * 4;
     const void *ins[] = {q, k, v};
@@ -353,8 +358,10 @@ int fa_fwd_masked(const void *q, const void *k, const void *v, void *o, float *l
     prm.H = H;
     prm.N = N;
     prm.cs = scale * kLog2e;
-    prm.wl = window_left < 0 ? -1 : window_left;
-    prm.wr = window_right < 0 ? -1 : window_right;
+    // an edge at N - 1 or beyond hides no key: clamp it there, so that the
+    // kernel's index arithmetic (row + edge) stays far from overflow
+    prm.wl = window_left < 0 ? -1 : (window_left < N ? window_left : N - 1);
+    prm.wr = window_right < 0 ? -1 : (window_right < N ? window_right : N - 1);
     prm.alibi = alibi_slopes;
     prm.inv_scale = 1.0f / scale;
     const int rows_per_tile = tile_rows_for(d);

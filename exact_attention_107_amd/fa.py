@@ -421,6 +421,8 @@ def fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, vt8: torch.Tensor, descale_q: to
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if lse is None else lse
     _check(out, "out", torch.bfloat16, dev)
     _check(lse, "lse", torch.float32, dev)
+    if tuple(out.shape) != (B, N, H, d) or tuple(lse.shape) != (B, H, N):
+        raise ValueError(f"out must be {(B, N, H, d)} and lse {(B, H, N)}")
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
         rc = lib.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), descale_q.data_ptr(),
@@ -456,6 +458,8 @@ def fwd_masked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, window_left
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if lse is None else lse
     _check(out, "out", torch.bfloat16, dev)
     _check(lse, "lse", torch.float32, dev)
+    if tuple(out.shape) != (B, N, H, d) or tuple(lse.shape) != (B, H, N):
+        raise ValueError(f"out must be {(B, N, H, d)} and lse {(B, H, N)}")
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
         rc = lib.fa_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),

@@ -270,12 +270,16 @@ int fa_fwd_rescale_counts(const void *q, const void *k, const void *v, void *o,
  *   window_left, window_right   key j is visible to query i iff
  *                  i - window_left <= j <= i + window_right; a negative value
  *                  leaves that side unbounded (window_right = 0 with an
- *                  unbounded left side is the causal mask).  Key tiles that
- *                  no row of a workgroup sees are skipped.
+ *                  unbounded left side is the causal mask); an edge of N - 1
+ *                  or more hides no key and is taken as N - 1 (so INT_MAX
+ *                  also means unbounded).  Key tiles that no row of a
+ *                  workgroup sees are skipped.
  *   alibi_slopes   NULL, or device fp32 [H]: slope_h * (j - i) is added to
  *                  the scaled score (ALiBi).
- * Every other argument as fa_fwd (no cu_seqlens, no causal flag).  Uses
- * hardware exp and the threshold rescale; every tile goes through the mask.
+ * Every other argument as fa_fwd (no cu_seqlens, no causal flag); N is at
+ * most 2^30 (FA_ERR_SHAPE beyond).  Uses hardware exp and the threshold
+ * rescale; tiles that a window edge cuts, the sequence tail, and every tile
+ * when a bias is given go through the mask step.
  */
 int fa_fwd_masked(const void *q, const void *k, const void *v, void *o,
                   float *lse, int B, int H, int N, int d, float scale,

@@ -105,6 +105,28 @@ def test_python_binding_checks():
         fa.fwd(x, x, x)  # not a GPU tensor
 
 
+def test_binding_rejects_undersized_outputs():
+    """Caller-given outputs of the FP8 and masked entry points must have the
+    full shapes; a smaller buffer is refused before the library is called
+    (the tensors here are host tensors, so nothing may reach a kernel)."""
+    import torch
+    B, N, H, d = 1, 100, 2, 64
+    q8 = torch.zeros(B, N, H, d, dtype=torch.uint8)
+    vt8 = torch.zeros(B, H, d, fa.fp8_vt_stride(N), dtype=torch.uint8)
+    ds = torch.ones(B, H, dtype=torch.float32)
+    o_ok = torch.empty(B, N, H, d, dtype=torch.bfloat16)
+    l_ok = torch.empty(B, H, N, dtype=torch.float32)
+    o_small = torch.empty(B, N - 1, H, d, dtype=torch.bfloat16)
+    l_small = torch.empty(B, H, N - 1, dtype=torch.float32)
+    for o, l in ((o_small, l_ok), (o_ok, l_small)):
+        with pytest.raises(ValueError, match="out must be"):
+            fa.fwd_fp8(q8, q8, vt8, ds, ds, ds, out=o, lse=l)
+    x = torch.zeros(B, N, H, d, dtype=torch.bfloat16)
+    for o, l in ((o_small, l_ok), (o_ok, l_small), (o_ok.view(B, N, d, H), l_ok)):
+        with pytest.raises(ValueError, match="out must be"):
+            fa.fwd_masked(x, x, x, window_left=3, out=o, lse=l)
+
+
 # workspaces for the split-KV calls (fake addresses, far from the others)
 OP, LP = 0x10000000, 0x20000000
 
@@ -252,3 +274,22 @@ def call_counts(lib, counts=0x700000, d=128, rescale_mode=2, **kw):
 ])
 def test_rescale_counts_invalid_arguments_are_rejected(lib, kw, code):
     assert call_counts(lib, **kw) == code
+
+
+def call_masked(lib, q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, N=100, d=128, scale=0.125, wl=-1, wr=0,
+                alibi=None):
+    return lib.fa_fwd_masked(*(ctypes.c_void_p(x) for x in (q, k, v, o, lse)), B, H, N, d,
+                             ctypes.c_float(scale), wl, wr, None if alibi is None else ctypes.c_void_p(alibi),
+                             None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), NULLPTR), (dict(lse=0), NULLPTR), (dict(N=0), SHAPE), (dict(d=96), HEAD_DIM),
+    (dict(scale=float("inf")), SCALE), (dict(alibi=0x700002), ALIGN), (dict(o=V), ALIAS),
+    (dict(alibi=O + 64), ALIAS),
+    # the window arithmetic is 32-bit: sequences up to 2^30 keys
+    (dict(B=1, H=1, d=64, N=(1 << 30) + 1, q=1 << 40, k=2 << 40, v=3 << 40, o=4 << 40, lse=5 << 40),
+     SHAPE),
+])
+def test_masked_invalid_arguments_are_rejected(lib, kw, code):
+    assert call_masked(lib, **kw) == code

@@ -76,3 +76,20 @@ def test_masked_rejects_bad_arguments():
     q = torch.zeros(1, 64, 1, 96, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(fa.FaError):
         fa.fwd_masked(q, q.clone(), q.clone(), window_left=4, window_right=0)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_masked_huge_window_edges_mean_unbounded(d):
+    """An edge of N - 1 or more hides no key: INT_MAX (and N, N + 5) on either
+    side give bitwise the result of an unbounded side."""
+    inp = make_inputs(Run("mkw", 2, 2, 300, d, False, 94))
+    big = 2 ** 31 - 1
+    ref = _run(inp, -1, -1, None)
+    ref_c = _run(inp, -1, 0, None)
+    for left, right, r in ((big, big, ref), (-1, big, ref), (big, -1, ref), (300, 305, ref), (big, 0, ref_c),
+                           (299, 0, ref_c)):
+        o, lse = _run(inp, left, right, None)
+        assert torch.equal(o.view(torch.int16), r[0].view(torch.int16)), (left, right)
+        assert torch.equal(lse, r[1]), (left, right)
+    ro, rl = omods.attention(inp["q"], inp["k"], inp["v"], scale=inp["scale"], left=-1, right=-1, slopes=None)
+    assert_within(metrics(from_dev(ref[0]), ref[1].cpu().numpy(), ro, rl), "unbounded window")
