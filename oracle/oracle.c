@@ -102,12 +102,31 @@ static void one_row(const struct job *jb, int64_t r, double *s)
         return;
     }
 
-    /* S_ij = scale * (q_i . k_j) */
-    for (int j = lo; j < hi; ++j) {
+    /* S_ij = scale * (q_i . k_j).  Each dot product is the plain sum over
+     * x = 0 .. d-1 in order; KB keys are summed side by side only so that
+     * the additions of different keys overlap in the CPU (every S_ij is
+     * bit-for-bit what the one-key-at-a-time loop gives). */
+    enum { KB = 8 };
+    double *qd = s + jb->N;     /* q_i widened once (the row buffer holds N + d) */
+    for (int x = 0; x < d; ++x) qd[x] = widen_bf16(qi[x]);
+    int j = lo;
+    for (; j + KB <= hi; j += KB) {
+        const uint16_t *kj[KB];
+        double dot[KB];
+        for (int u = 0; u < KB; ++u) {
+            kj[u] = jb->k + ((t0 + j + u) * H + h) * (int64_t)d;
+            dot[u] = 0.0;
+        }
+        for (int x = 0; x < d; ++x)
+            for (int u = 0; u < KB; ++u)
+                dot[u] += qd[x] * widen_bf16(kj[u][x]);
+        for (int u = 0; u < KB; ++u) s[j + u] = jb->scale * dot[u];
+    }
+    for (; j < hi; ++j) {
         const uint16_t *kj = jb->k + ((t0 + j) * H + h) * (int64_t)d;
         double dot = 0.0;
         for (int x = 0; x < d; ++x)
-            dot += widen_bf16(qi[x]) * widen_bf16(kj[x]);
+            dot += qd[x] * widen_bf16(kj[x]);
         s[j] = jb->scale * dot;
     }
 
@@ -135,7 +154,8 @@ static void one_row(const struct job *jb, int64_t r, double *s)
 static void *worker(void *arg)
 {
     struct job *jb = (struct job *)arg;
-    double *s = (double *)malloc(sizeof(double) * (size_t)(jb->N > 0 ? jb->N : 1));
+    /* one score row (N) and the widened query row (d) */
+    double *s = (double *)malloc(sizeof(double) * ((size_t)(jb->N > 0 ? jb->N : 1) + (size_t)jb->d));
     if (!s) {
         jb->status = ORACLE_ERR_ALLOC;
         return NULL;

@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 
 import oracle
+from oracle import matrix
 from oracle_pins import ALL_PINS
 from oracle.online import online_attention
 from exact_attention_107_amd.workloads import RUNS, make_inputs
@@ -13,6 +14,52 @@ from exact_attention_107_amd.workloads import RUNS, make_inputs
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
 def test_oracle_pin(pin, oracle_lib):
     pin(functools.partial(oracle.attention, lib=oracle_lib))
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
+def test_matrix_oracle_pin(pin):
+    """The whole-matrix form of the oracle (oracle.matrix, used for the
+    every-row checks of full-size GPU outputs) against the same pins."""
+    pin(matrix.attention)
+
+
+@pytest.mark.parametrize("case", ["dense", "causal", "packed", "d64", "d256", "wide", "range"])
+def test_matrix_oracle_equals_c_oracle(case, oracle_lib):
+    """The two forms of the definition agree to fp64 rounding on shapes with
+    several row blocks, ragged ends, empty and one-token sequences."""
+    from exact_attention_107_amd.workloads import Run
+    kw = {}
+    if case == "packed":
+        inp = make_inputs(Run("p", 1, 3, 0, 128, True, 5), lengths=[0, 1, 1500, 77, 0, 2100])
+    else:
+        d = {"d64": 64, "d256": 256}.get(case, 128)
+        causal = case in ("causal", "range")
+        sig, boost = (3.0, 0.01) if case == "wide" else (1.0, 0.0)
+        inp = make_inputs(Run("m", 2, 2, 1300, d, causal, 6, sigma_qk=sig, boost_frac=boost))
+        if case == "range":
+            kw["key_range"] = (200, 1100)
+    args = (inp["q"], inp["k"], inp["v"])
+    c = dict(scale=inp["scale"], causal=inp["causal"], cu_seqlens=inp["cu_seqlens"], **kw)
+    o1, l1 = oracle.attention(*args, lib=oracle_lib, **c)
+    o2, l2 = matrix.attention(*args, **c)
+    assert np.array_equal(np.isfinite(l1), np.isfinite(l2))
+    fin = np.isfinite(l1)
+    assert np.max(np.abs(o1 - o2)) < 1e-12
+    assert np.max(np.abs(l1[fin] - l2[fin])) < 1e-12
+
+
+def test_matrix_oracle_iter_heads_equals_attention():
+    from exact_attention_107_amd.workloads import Run
+    inp = make_inputs(Run("p", 1, 2, 0, 64, True, 8), lengths=[5, 0, 700])
+    o, lse = matrix.attention(inp["q"], inp["k"], inp["v"], scale=inp["scale"], causal=True,
+                              cu_seqlens=inp["cu_seqlens"])
+    cu = inp["cu_seqlens"]
+    seen = 0
+    for b, h, ob, lb in matrix.iter_heads(inp["q"], inp["k"], inp["v"], scale=inp["scale"], causal=True,
+                                          cu_seqlens=cu):
+        assert np.array_equal(ob, o[cu[b]:cu[b + 1], h]) and np.array_equal(lb, lse[h, cu[b]:cu[b + 1]])
+        seen += 1
+    assert seen == 3 * 2
 
 
 def test_online_rescale_counts():

@@ -35,8 +35,16 @@ MUTANTS = {
                            "const uint16_t *qi = jb->q + ((t0 + i) * H + 0) * (int64_t)d;"),
     "value_row_of_query": ("const uint16_t *vj = jb->v + ((t0 + j) * H + h) * (int64_t)d;",
                            "const uint16_t *vj = jb->v + ((t0 + i) * H + h) * (int64_t)d;"),
-    "dot_drops_last_dim": ("for (int x = 0; x < d; ++x)\n            dot +=",
-                           "for (int x = 0; x < d - 1; ++x)\n            dot +="),
+    "dot_drops_last_dim": ("for (int x = 0; x < d; ++x)\n            for (int u = 0; u < KB; ++u)",
+                           "for (int x = 0; x < d - 1; ++x)\n            for (int u = 0; u < KB; ++u)"),
+    "dot_drops_last_dim_tail": ("for (int x = 0; x < d; ++x)\n            dot +=",
+                                "for (int x = 0; x < d - 1; ++x)\n            dot +="),
+    "key_block_one_row": ("kj[u] = jb->k + ((t0 + j + u) * H + h)", "kj[u] = jb->k + ((t0 + j) * H + h)"),
+    "key_block_q_as_key": ("kj[u] = jb->k + ((t0 + j + u)", "kj[u] = jb->q + ((t0 + j + u)"),
+    "key_block_scale_dropped": ("for (int u = 0; u < KB; ++u) s[j + u] = jb->scale * dot[u];",
+                                "for (int u = 0; u < KB; ++u) s[j + u] = dot[u];"),
+    "query_dims_swapped": ("for (int x = 0; x < d; ++x) qd[x] = widen_bf16(qi[x]);",
+                                 "for (int x = 0; x < d; ++x) qd[x] = widen_bf16(qi[x ^ 1]);"),
     "packed_ignores_offset": ("*start = jb->cu[b];", "*start = 0;"),
     "range_high_inclusive": ("const int hi = jb->kv_hi < nvis ? jb->kv_hi : nvis;",
                              "const int hi = jb->kv_hi + 1 < nvis ? jb->kv_hi + 1 : nvis;"),
@@ -92,3 +100,42 @@ def test_merge_mutant_is_caught(name, monkeypatch, oracle_lib):
     attn = functools.partial(oracle.attention, lib=oracle_lib)
     with np.errstate(all="ignore"), pytest.raises(AssertionError):
         oracle_pins.pin_key_range_partition_merge(attn)
+
+
+MATRIX_SRC = os.path.join(os.path.dirname(oracle.__file__), "matrix.py")
+MATRIX_MUTANTS = {
+    "causal_upper": ("keys[None, :k_end - lo] > ri[:, None]", "keys[None, :k_end - lo] < ri[:, None]"),
+    "causal_strict": ("keys[None, :k_end - lo] > ri[:, None]", "keys[None, :k_end - lo] >= ri[:, None]"),
+    "no_scale": ("S = (qh[ri] @ kh[lo:k_end].T) * sc", "S = qh[ri] @ kh[lo:k_end].T"),
+    "unnormalised": ("ob = (E / torch.where(seen, l, torch.ones_like(l))[:, None]) @ vh[lo:k_end]",
+                     "ob = E @ vh[lo:k_end]"),
+    "lse_without_max": ("torch.where(seen, m + torch.log(l), m)", "torch.where(seen, torch.log(l), m)"),
+    "k_as_value": ("@ vh[lo:k_end]", "@ kh[lo:k_end]"),
+    "range_ignores_low": ("lo, hi = (0, n) if key_range is None else (max(0, int(key_range[0])),",
+                          "lo, hi = (0, n) if key_range is None else (0,"),
+    "causal_keys_stop_early": ("k_end = min(hi, int(ri.max()) + 1) if causal else hi",
+                               "k_end = min(hi, int(ri.max())) if causal else hi"),
+    "packed_ignores_offset": ("return torch.from_numpy(_widen(flat[t0:t0 + n, h, :]))",
+                              "return torch.from_numpy(_widen(flat[0:n, h, :]))"),
+    "head_zero": ("return torch.from_numpy(_widen(flat[t0:t0 + n, h, :]))",
+                  "return torch.from_numpy(_widen(flat[t0:t0 + n, 0, :]))"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MATRIX_MUTANTS))
+def test_matrix_mutant_is_caught(name):
+    """The same pins catch plausible mistakes in the whole-matrix form."""
+    import types
+    old, new = MATRIX_MUTANTS[name]
+    src = open(MATRIX_SRC).read().replace("from . import _widen, all_rows", "from oracle import _widen, all_rows")
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mod = types.ModuleType(f"matrix_{name}")
+    exec(compile(src.replace(old, new), f"matrix_{name}.py", "exec"), mod.__dict__)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(mod.attention)
+        except (AssertionError, RuntimeError, FloatingPointError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"
