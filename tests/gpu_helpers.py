@@ -104,3 +104,40 @@ def sampled_parity(inp, o, lse, count=384, seed=0):
                                       rows=rows)
     og, lg = gather_rows(inp, o, lse, rows)
     return metrics(og, lg, o_ref, lse_ref)
+
+
+def every_row_parity(inp, o: torch.Tensor, lse: torch.Tensor):
+    """Every row of a full-size output against the fp64 oracle in its
+    whole-matrix form (oracle.matrix), one (sequence, head) at a time.
+    Returns the metrics over all elements and the worst head."""
+    from oracle import matrix
+    o_bits = o.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    lse_h = lse.cpu().numpy().astype(np.float64)
+    cu = inp.get("cu_seqlens")
+    max_o = max_l = 0.0
+    sum_o = 0.0
+    count = 0
+    finite = True
+    worst = None
+    for b, h, o_ref, l_ref in matrix.iter_heads(inp["q"], inp["k"], inp["v"], scale=inp["scale"],
+                                                causal=inp["causal"], cu_seqlens=cu):
+        if cu is None:
+            og = bf16_to_f32(o_bits[b, :, h, :]).astype(np.float64)
+            lg = lse_h[b, h, :]
+        else:
+            t0, t1 = int(cu[b]), int(cu[b + 1])
+            og = bf16_to_f32(o_bits[t0:t1, h, :]).astype(np.float64)
+            lg = lse_h[h, t0:t1]
+        if og.size == 0:
+            continue
+        do = np.abs(og - o_ref)
+        dl = np.abs(lg - l_ref)
+        finite = finite and bool(np.all(np.isfinite(og)) and np.all(np.isfinite(lg)))
+        mo, ml = float(do.max()), float(dl.max())
+        if worst is None or mo > worst[2]:
+            worst = (b, h, mo)
+        max_o, max_l = max(max_o, mo), max(max_l, ml)
+        sum_o += float(do.sum())
+        count += do.size
+    return {"max_o": max_o, "mean_o": sum_o / max(count, 1), "max_lse": max_l, "finite": finite,
+            "elements": count, "worst_head": worst}
