@@ -125,3 +125,23 @@ def test_planted_mistakes_are_caught(monkeypatch, oracle_lib):
                         lambda q8, k8, vt8, dq, dk, dv, **kw: good_attention(q8, k8, vt8, dq, dk, np.ones_like(dv), **kw))
     with pytest.raises(AssertionError):
         test_attention_matches_c_oracle_on_exact_inputs(False, oracle_lib)
+
+
+def test_quantize_step_order_pinned_by_hand_derived_codes():
+    """The quantisation reading fixes the fp32 step order: codes are
+    E4M3(x * fp32(1 / descale)), not E4M3(x * fp32(448 / amax)).  The golden
+    cases (tests/golden/make_fp8_quant_cases.py, derived with struct's fp32
+    rounding and exact rationals) are pairs where the two orders round to
+    different codes."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "fp8_quant_cases.json")
+    cases = json.load(open(path))["cases"]
+    assert len(cases) >= 8
+    for c in cases:
+        x = np.array([int(c["amax_bf16"], 16), int(c["x_bf16"], 16)], dtype=np.uint16).reshape(1, 1, 1, 2)
+        codes, descale = fp8.quantize(x)
+        assert float(descale[0, 0]) == c["descale_fp32"]
+        assert int(codes[0, 0, 0, 1]) == c["code"], c
+        assert int(codes[0, 0, 0, 1]) != c["code_alternative"]
+        assert int(codes[0, 0, 0, 0]) == 0x7E          # amax itself maps to 448
