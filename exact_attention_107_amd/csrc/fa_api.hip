@@ -6,10 +6,18 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fa.h"
 #include "fa_internal.h"
 
 using namespace fa_detail;
+
+// Scratch of fa_fwd_splitkv_static (the split partials: o_part, then
+// lse_part).  Every GPU the library runs on holds its own copy until the
+// process ends.  In host code `scratch` is only a stand-in for the symbol:
+// its device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) char scratch[FA_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -40,6 +48,25 @@ int key_tiles(int N) { return (N + kTileKeys - 1) / kTileKeys; }
 // N after clamping) plus a tile must fit in an int.
 constexpr int kMaskedMaxN = 1 << 30;
 
+// Device address of the current GPU's scratch array, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+int scratch_for_current_device(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return FA_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -56,6 +83,7 @@ const char *fa_strerror(int code) {
         case FA_ERR_ALIAS: return "an output overlaps an input or the other output";
         case FA_ERR_HIP: return "HIP kernel launch failed";
         case FA_ERR_SPLIT: return "num_splits out of range (1 .. ceil(N / tile keys))";
+        case FA_ERR_SCRATCH: return "the split partials exceed the static scratch (FA_STATIC_SCRATCH_BYTES)";
         default: return "unknown fa status code";
     }
 }
@@ -189,31 +217,34 @@ int fa_merge(const float *o_part, const float *lse_part, int num_splits, int B, 
     return launch_merge(mp, d, stream) == 0 ? FA_OK : FA_ERR_HIP;
 }
 
-int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
-                   int N, int d, float scale, int causal, int num_splits, float *o_part,
-                   float *lse_part, hipStream_t stream) {
-    if (!q || !k || !v || !o || !lse || !o_part || !lse_part) return FA_ERR_NULLPTR;
+// Validation shared by the two split-KV entry points (everything but the
+// workspaces).
+static int splitkv_check(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
+                         int d, float scale, int num_splits) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULLPTR;
     if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
     if (d != 64 && d != 128 && d != 256) return FA_ERR_HEAD_DIM;
     if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_SCALE;
     if (num_splits < 1 || num_splits > key_tiles(N)) return FA_ERR_SPLIT;
-    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
-        misaligned(o_part, 16) || misaligned(lse, 4) || misaligned(lse_part, 4))
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) || misaligned(lse, 4))
         return FA_ERR_ALIGN;
     const long long rows = static_cast<long long>(B) * N * H;
     const long long elems = rows * d;
     if (elems <= 0 || elems * num_splits > (1LL << 46) || !token_stride_ok(H, d)) return FA_ERR_SHAPE;
     const size_t tb = static_cast<size_t>(elems) * 2, lb = static_cast<size_t>(rows) * 4;
-    const size_t opb = static_cast<size_t>(elems) * num_splits * 4, lpb = static_cast<size_t>(rows) * num_splits * 4;
     const void *ins[3] = {q, k, v};
     for (const void *in : ins)
-        if (overlap(o, tb, in, tb) || overlap(lse, lb, in, tb) || overlap(o_part, opb, in, tb) ||
-            overlap(lse_part, lpb, in, tb))
-            return FA_ERR_ALIAS;
-    if (overlap(o, tb, lse, lb) || overlap(o_part, opb, o, tb) || overlap(o_part, opb, lse, lb) ||
-        overlap(lse_part, lpb, o, tb) || overlap(lse_part, lpb, lse, lb) || overlap(o_part, opb, lse_part, lpb))
-        return FA_ERR_ALIAS;
+        if (overlap(o, tb, in, tb) || overlap(lse, lb, in, tb)) return FA_ERR_ALIAS;
+    if (overlap(o, tb, lse, lb)) return FA_ERR_ALIAS;
+    return FA_OK;
+}
 
+// The split forward and the merge on validated arguments.
+static int splitkv_launch(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
+                          int d, float scale, int causal, int num_splits, float *o_part, float *lse_part,
+                          hipStream_t stream) {
+    const long long rows = static_cast<long long>(B) * N * H;
+    const long long elems = rows * d;
     Params prm{};
     prm.q = static_cast<const uint16_t *>(q);
     prm.k = static_cast<const uint16_t *>(k);
@@ -256,6 +287,43 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
     mp.N = N;
     mp.nsplit = num_splits;
     return launch_merge(mp, d, stream) == 0 ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                   int N, int d, float scale, int causal, int num_splits, float *o_part,
+                   float *lse_part, hipStream_t stream) {
+    if (!o_part || !lse_part) return FA_ERR_NULLPTR;
+    const int rc = splitkv_check(q, k, v, o, lse, B, H, N, d, scale, num_splits);
+    if (rc != FA_OK) return rc;
+    if (misaligned(o_part, 16) || misaligned(lse_part, 4)) return FA_ERR_ALIGN;
+    const long long rows = static_cast<long long>(B) * N * H;
+    const long long elems = rows * d;
+    const size_t tb = static_cast<size_t>(elems) * 2, lb = static_cast<size_t>(rows) * 4;
+    const size_t opb = static_cast<size_t>(elems) * num_splits * 4, lpb = static_cast<size_t>(rows) * num_splits * 4;
+    const void *ins[3] = {q, k, v};
+    for (const void *in : ins)
+        if (overlap(o_part, opb, in, tb) || overlap(lse_part, lpb, in, tb)) return FA_ERR_ALIAS;
+    if (overlap(o_part, opb, o, tb) || overlap(o_part, opb, lse, lb) || overlap(lse_part, lpb, o, tb) ||
+        overlap(lse_part, lpb, lse, lb) || overlap(o_part, opb, lse_part, lpb))
+        return FA_ERR_ALIAS;
+    return splitkv_launch(q, k, v, o, lse, B, H, N, d, scale, causal, num_splits, o_part, lse_part, stream);
+}
+
+int fa_fwd_splitkv_static(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                          int N, int d, float scale, int causal, int num_splits, hipStream_t stream) {
+    const int rc = splitkv_check(q, k, v, o, lse, B, H, N, d, scale, num_splits);
+    if (rc != FA_OK) return rc;
+    // partials: o_part [S, B, N, H, d] then lse_part [S, B, H, N], fp32;
+    // rows * d * 4 is a multiple of 256, so lse_part stays aligned
+    const long long rows = static_cast<long long>(B) * N * H;
+    const long long need = static_cast<long long>(num_splits) * rows * (d + 1) * 4;
+    if (need > static_cast<long long>(FA_STATIC_SCRATCH_BYTES)) return FA_ERR_SCRATCH;
+    void *base = nullptr;
+    const int sc = scratch_for_current_device(&base);
+    if (sc != FA_OK) return sc;
+    float *o_part = static_cast<float *>(base);
+    float *lse_part = o_part + static_cast<long long>(num_splits) * rows * d;
+    return splitkv_launch(q, k, v, o, lse, B, H, N, d, scale, causal, num_splits, o_part, lse_part, stream);
 }
 
 long long fa_bwd_workspace_floats(int B, int H, int N) {

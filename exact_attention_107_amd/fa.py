@@ -22,7 +22,9 @@ RESCALE_ALWAYS, RESCALE_STRICT, RESCALE_THRESHOLD = 0, 1, 2
 EXPORTS = ("fa_fwd", "fa_fwd_variant", "fa_strerror", "fa_tile_rows", "fa_tile_keys",
            "fa_fwd_splitkv", "fa_merge", "fa_split_range", "fa_num_splits", "fa_bwd",
            "fa_bwd_workspace_floats", "fa_fwd_fp8", "fa_quantize_fp8", "fa_fp8_vt_stride",
-           "fa_fwd_masked", "fa_fwd_rescale_counts")
+           "fa_fwd_masked", "fa_fwd_rescale_counts", "fa_fwd_splitkv_static")
+FA_ERR_SCRATCH = 10
+STATIC_SCRATCH_BYTES = 64 << 20   # FA_STATIC_SCRATCH_BYTES of include/fa.h
 
 _lib = None
 
@@ -57,6 +59,9 @@ def load(path: str | None = None):
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_float, i32,
                                    i32, vp, vp, vp]
     lib.fa_fwd_splitkv.restype = i32
+    lib.fa_fwd_splitkv_static.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_float, i32,
+                                          i32, vp]
+    lib.fa_fwd_splitkv_static.restype = i32
     lib.fa_merge.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
     lib.fa_merge.restype = i32
     lib.fa_split_range.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
@@ -267,6 +272,44 @@ def fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bo
         rc = lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                 B, H, N, d, ctypes.c_float(scale), int(bool(causal)), S,
                                 o_part.data_ptr(), lse_part.data_ptr(), ctypes.c_void_p(s.cuda_stream))
+    if rc != 0:
+        raise FaError(rc, strerror(rc))
+    return out, lse
+
+
+def fwd_splitkv_static(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+                       scale: float | None = None, splits: int | None = None,
+                       out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                       stream: torch.cuda.Stream | None = None):
+    """``fa_fwd_splitkv_static``: the split-KV forward with its partials in
+    the library's static per-GPU scratch (the C call allocates nothing; pass
+    ``out`` and ``lse`` to allocate nothing here either).  Calls that overlap
+    on one GPU race.  Returns ``(o, lse)``."""
+    lib = load()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a GPU tensor")
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, name, torch.bfloat16, dev)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must have the same shape")
+    B, N, H, d = _dense_shape(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if splits is None:
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        splits = num_splits(B, H, N, d, causal, cus)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if lse is None else lse
+    _check(out, "out", torch.bfloat16, dev)
+    _check(lse, "lse", torch.float32, dev)
+    if tuple(out.shape) != (B, N, H, d) or tuple(lse.shape) != (B, H, N):
+        raise ValueError(f"out must be {(B, N, H, d)} and lse {(B, H, N)}")
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = lib.fa_fwd_splitkv_static(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                       lse.data_ptr(), B, H, N, d, ctypes.c_float(scale),
+                                       int(bool(causal)), int(splits), ctypes.c_void_p(s.cuda_stream))
     if rc != 0:
         raise FaError(rc, strerror(rc))
     return out, lse

@@ -69,7 +69,8 @@ enum fa_status {
     FA_ERR_VARIANT = 6,  /* exp_mode or rescale_mode out of range               */
     FA_ERR_ALIAS = 7,    /* o or lse overlaps an input or each other            */
     FA_ERR_HIP = 8,      /* the HIP launch itself failed                        */
-    FA_ERR_SPLIT = 9     /* num_splits outside 1 .. ceil(N / fa_tile_keys(d))   */
+    FA_ERR_SPLIT = 9,    /* num_splits outside 1 .. ceil(N / fa_tile_keys(d))   */
+    FA_ERR_SCRATCH = 10  /* fa_fwd_splitkv_static: partials exceed its scratch  */
 };
 
 /* How P~ = exp(s - m) is evaluated (section 3.2 of the FlashAttention V4
@@ -165,6 +166,31 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o,
                    float *lse, int B, int H, int N, int d, float scale,
                    int causal, int num_splits, float *o_part, float *lse_part,
                    hipStream_t stream);
+
+/* Size of the static scratch of fa_fwd_splitkv_static, per GPU: 64 MiB. */
+#define FA_STATIC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * fa_fwd_splitkv_static: fa_fwd_splitkv for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The split partials live in a static
+ * device array of FA_STATIC_SCRATCH_BYTES that each GPU the library runs on
+ * holds until the process ends (its address is looked up once per device,
+ * on that device's first call, with the caller's device current); the call
+ * itself allocates and frees nothing.
+ *   Arguments as fa_fwd_splitkv without o_part / lse_part.  The partials
+ *   take num_splits * B * N * H * (d + 1) * 4 bytes; more than
+ *   FA_STATIC_SCRATCH_BYTES returns FA_ERR_SCRATCH before any HIP call.
+ * Results are bitwise those of fa_fwd_splitkv (the same kernels).  Every
+ * call on one GPU shares that GPU's scratch and leaves its partials there
+ * (each call writes every partial it reads, so nothing needs clearing):
+ * calls that overlap on one GPU -- on different streams, or from several
+ * threads -- race, and the caller must order them.
+ */
+int fa_fwd_splitkv_static(const void *q, const void *k, const void *v,
+                          void *o, float *lse, int B, int H, int N, int d,
+                          float scale, int causal, int num_splits,
+                          hipStream_t stream);
 
 /*
  * fa_merge: the combination step of fa_fwd_splitkv, usable on its own (for

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
 
 # fa_status codes of include/fa.h
-OK, NULLPTR, SHAPE, HEAD_DIM, SCALE, ALIGN, VARIANT, ALIAS, HIP, SPLIT = range(10)
+OK, NULLPTR, SHAPE, HEAD_DIM, SCALE, ALIGN, VARIANT, ALIAS, HIP, SPLIT, SCRATCH = range(11)
 
 
 def header_functions():
@@ -46,7 +46,7 @@ def test_exports_every_header_function(lib):
 def test_enum_values_match_binding():
     st = header_enum("fa_status")
     assert st["FA_OK"] == OK and st["FA_ERR_HIP"] == HIP and st["FA_ERR_ALIAS"] == ALIAS
-    assert st["FA_ERR_SPLIT"] == SPLIT and len(st) == 10
+    assert st["FA_ERR_SPLIT"] == SPLIT and st["FA_ERR_SCRATCH"] == SCRATCH and len(st) == 11
     ex = header_enum("fa_exp_mode")
     assert (ex["FA_EXP_HW"], ex["FA_EXP_POLY"], ex["FA_EXP_MIXED"]) == (fa.EXP_HW, fa.EXP_POLY, fa.EXP_MIXED)
     rs = header_enum("fa_rescale_mode")
@@ -55,7 +55,7 @@ def test_enum_values_match_binding():
 
 
 def test_strerror(lib):
-    for code in range(10):
+    for code in range(11):
         s = fa.strerror(code)
         assert isinstance(s, str) and s
     assert "unknown" in fa.strerror(1234)
@@ -149,6 +149,36 @@ def call_split(lib, q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, N=1000, d=128, scale=0.
 ])
 def test_splitkv_invalid_arguments_are_rejected(lib, kw, code):
     assert call_split(lib, **kw) == code
+
+
+def call_split_static(lib, q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, N=1000, d=128, scale=0.125, causal=0,
+                      splits=4):
+    return lib.fa_fwd_splitkv_static(ctypes.c_void_p(q), ctypes.c_void_p(k), ctypes.c_void_p(v),
+                                     ctypes.c_void_p(o), ctypes.c_void_p(lse), B, H, N, d,
+                                     ctypes.c_float(scale), causal, splits, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), NULLPTR), (dict(lse=0), NULLPTR), (dict(B=0), SHAPE), (dict(d=32), HEAD_DIM),
+    (dict(scale=float("nan")), SCALE), (dict(splits=0), SPLIT), (dict(splits=17), SPLIT),
+    (dict(o=O + 8), ALIGN), (dict(o=Q), ALIAS), (dict(lse=V + 64), ALIAS),
+    # partials of S * B * N * H * (d + 1) * 4 bytes must fit the 64 MiB scratch:
+    # 2 * 16384 * 4 * 129 * 4 = 64.5 MiB does not; 2 * 16000 * 4 * 129 * 4 = 63.0 MiB does (a GPU test)
+    (dict(B=1, H=4, N=16384, d=128, splits=2, q=1 << 40, k=2 << 40, v=3 << 40, o=4 << 40, lse=5 << 40),
+     SCRATCH),
+    (dict(B=1, H=32, N=16384, d=128, splits=2, q=1 << 40, k=2 << 40, v=3 << 40, o=4 << 40, lse=5 << 40),
+     SCRATCH),
+])
+def test_splitkv_static_invalid_arguments_are_rejected(lib, kw, code):
+    """Rejected before any HIP call (so also here, without a GPU); a request
+    larger than the static scratch gets its own code."""
+    assert call_split_static(lib, **kw) == code
+
+
+def test_static_scratch_size_matches_header():
+    txt = open(HEADER).read()
+    assert "#define FA_STATIC_SCRATCH_BYTES (64u << 20)" in txt
+    assert fa.STATIC_SCRATCH_BYTES == 64 << 20
 
 
 def call_merge(lib, op=OP, lp=LP, splits=3, B=1, H=2, N=100, d=64, o=O, lse=L):
