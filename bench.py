@@ -32,6 +32,19 @@ KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_107_amd", "csrc", f)
                  [os.path.join(ROOT, "exact_attention_107_amd", "build.py")]
 
 
+def workload_label(run, inp) -> str:
+    """What the run is, with its sizes and input distribution."""
+    if inp.get("cu_seqlens") is not None:
+        shape = (f"{len(inp['lengths'])} packed sequences of {run.len_lo}..{run.len_hi} tokens "
+                 f"(T={inp['T']}) H={inp['H']} d={inp['d']}")
+    else:
+        shape = f"B={inp['B']} H={inp['H']} N={inp['N']} d={inp['d']}"
+    dist = f"Q,K~N(0,{run.sigma_qk:g}^2)"
+    if run.boost_frac > 0:
+        dist += f" with {run.boost_frac:.0%} of K rows x8"
+    return f"{run.name}: {shape} causal={inp['causal']} {dist}, V~N(0,1)"
+
+
 def kernel_fingerprint() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
@@ -46,6 +59,21 @@ def log(msg: str) -> None:
 
 def to_dev(bits, torch):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def settle_clock(launch, seconds: float, torch) -> int:
+    """Repeat `launch` for about `seconds` of wall time before anything is
+    timed: the GPU leaves its idle clock over the first tens of
+    milliseconds of load, which a short warmup alone does not cover.
+    Returns the number of launches (reported in the JSON line)."""
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(5):
+            launch()
+        torch.cuda.synchronize()
+        n += 5
+    return n
 
 
 def time_launches(launch, steps: int, warmup: int, torch):
@@ -355,6 +383,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="bwd: time only the backward pass of --workload (for profiling)")
+    ap.add_argument("--settle-s", type=float, default=0.5,
+                    help="seconds of untimed launches before the warmup, so that the timed steps "
+                         "run at the clock the GPU holds under this load (0: none)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "
                          "reference dispatch for HBM byte counters)")
@@ -405,7 +436,9 @@ def main() -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    log(f"[bench] timing {args.steps} steps after {args.warmup} warmup")
+    settle_launches = settle_clock(launch, args.settle_s, torch) if args.settle_s > 0 else 0
+    log(f"[bench] timing {args.steps} steps after {args.warmup} warmup "
+        f"({settle_launches} launches to settle the clock first)")
     ms_step, ms_kernel, ms_med, ms_min = time_launches(launch, args.steps, args.warmup, torch)
     value = f / (ms_step * 1e-3) / 1e12
     achieved = f / (ms_kernel * 1e-3) / 1e12
@@ -418,11 +451,12 @@ def main() -> int:
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {
-            "workload": f"{run.name}: B={inp['B']} H={inp['H']} N={inp['N']} d={inp['d']} "
-                        f"causal={inp['causal']} Q,K~N(0,{run.sigma_qk}^2) 1% K rows x8, V~N(0,1)",
+            "workload": workload_label(run, inp),
             "B": inp["B"], "H": inp["H"], "N": inp["N"], "d": inp["d"], "causal": inp["causal"],
             "flops_per_step": f, "tile_rows": fa.tile_rows(inp["d"]), "tile_keys": fa.tile_keys(inp["d"]),
         },
+        "clock_settle": {"seconds": args.settle_s, "launches": settle_launches,
+                         "note": "untimed launches before the warmup steps"},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {
             "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
