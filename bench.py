@@ -505,6 +505,28 @@ def main() -> int:
                 variants[f"{en}/{rn}"] = {"ms": round(kms, 4),
                                           "tflops": round(f / (kms * 1e-3) / 1e12, 1)}
         out["variants"] = variants
+        # the two-group ping-pong schedule (fa_fwd_pingpong, d = 128): same
+        # arithmetic, the workgroup's halves half a key tile apart
+        pingpong = {}
+        for name in ("wide", "mid", "mid_causal", "long_causal", "varlen_causal"):
+            r = RUNS[name]
+            ri = make_inputs(r) if name != run.name else inp
+            rq, rk, rv = (to_dev(ri[x], torch) for x in ("q", "k", "v"))
+            rcu = torch.from_numpy(ri["cu_seqlens"]).cuda() if ri["cu_seqlens"] is not None else None
+            ro = torch.empty_like(rq)
+            rl_shape = (ri["H"], ri["T"]) if rcu is not None else (ri["B"], ri["H"], ri["N"])
+            rl = torch.empty(rl_shape, dtype=torch.float32, device="cuda")
+            rf = flops(ri["lengths"], ri["H"], ri["d"], ri["causal"])
+            res = {}
+            for sched, pp in (("in_step", False), ("pingpong", True)):
+                def plaunch():
+                    fa.fwd(rq, rk, rv, causal=ri["causal"], scale=ri["scale"], cu_seqlens=rcu, out=ro, lse=rl,
+                           pingpong=pp)
+                _, kms, _, _ = time_launches(plaunch, 30, 20, torch)
+                res[sched] = round(rf / (kms * 1e-3) / 1e12, 1)
+            pingpong[name] = res
+            del rq, rk, rv, ro, rl
+        out["pingpong_tflops"] = pingpong
         out["split_kv"] = split_kv_runs(torch, fa)
         out["backward"] = {name: backward_run(torch, fa, name)[0]
                            for name in ("mid", "mid_causal", "bwd_long", "bwd_long_causal", "varlen_causal")}

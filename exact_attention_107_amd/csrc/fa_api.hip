@@ -96,7 +96,8 @@ int fa_tile_keys(int d) { return (d == 64 || d == 128 || d == 256) ? kTileKeys :
 // instance (d = 128, hardware exp2) and receives its statistics.
 static int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
                     int N, int d, float scale, int causal, const int32_t *cu_seqlens,
-                    hipStream_t stream, int exp_mode, int rescale_mode, unsigned long long *counts) {
+                    hipStream_t stream, int exp_mode, int rescale_mode, unsigned long long *counts,
+                    bool ping = false) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULLPTR;
     if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
     if (d != 64 && d != 128 && d != 256) return FA_ERR_HEAD_DIM;
@@ -143,7 +144,8 @@ static int fwd_impl(const void *q, const void *k, const void *v, void *o, float 
 
     prm.counts = counts;
     KernelFn fn = counts ? select_count_d128(causal != 0, varlen, rescale_mode)
-                         : pick(d, causal != 0, varlen, exp_mode, rescale_mode);
+                         : (ping ? select_ping_d128(causal != 0, varlen)
+                                 : pick(d, causal != 0, varlen, exp_mode, rescale_mode));
     (void)hipGetLastError();  // clear a stale error so the check below is ours
     hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(grid)), dim3(waves_for(d) * 64), 0, stream, prm);
     if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
@@ -529,6 +531,13 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int
            int d, float scale, int causal, const int32_t *cu_seqlens, hipStream_t stream) {
     return fa_fwd_variant(q, k, v, o, lse, B, H, N, d, scale, causal, cu_seqlens, stream,
                           FA_EXP_HW, FA_RESCALE_STRICT);
+}
+
+int fa_fwd_pingpong(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
+                    int d, float scale, int causal, const int32_t *cu_seqlens, hipStream_t stream) {
+    if (d != 128 && (d == 64 || d == 256)) return FA_ERR_HEAD_DIM;
+    return fwd_impl(q, k, v, o, lse, B, H, N, d, scale, causal, cu_seqlens, stream, FA_EXP_HW, FA_RESCALE_STRICT,
+                    nullptr, d == 128);
 }
 
 int fa_fwd_rescale_counts(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,

@@ -79,6 +79,9 @@ KernelFn select_d128(bool causal, bool varlen, int exp_mode, int rescale_mode);
 KernelFn select_d256(bool causal, bool varlen, int exp_mode, int rescale_mode);
 // Instance that also counts rescales (head dimension 128, hardware exp2).
 KernelFn select_count_d128(bool causal, bool varlen, int rescale_mode);
+// The default forward (hardware exp2, strict rescale) with the two halves of
+// the eight-wave workgroup run half a key tile apart (head dimension 128).
+KernelFn select_ping_d128(bool causal, bool varlen);
 // Window-mask / linear-bias instance (dense layout).
 KernelFn select_mods_d64();
 KernelFn select_mods_d128();

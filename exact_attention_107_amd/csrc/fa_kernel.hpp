@@ -146,11 +146,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, lo
                                              0x00020000);
 }
 
-// Resource over rows row0 .. n-1 of a row-strided tensor (`row_bytes` apart,
-// element pointer `base` at row 0): rows at or past n read as zeros.
+// Resource over rows row0 .. min(n, row0 + 64) - 1 of a bf16 tensor whose
+// rows are row_elems elements apart (`base` points at row 0): rows at or
+// past n read as zeros.  No access through it reaches 64 rows past row0, and
+// row_elems * 2 <= 2^23 (the library's token-stride limit), so the size is
+// computed in 32-bit scalar arithmetic (a 64-bit clamp compiles to vector
+// compares feeding scalar selects, a slow chain in front of every load).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t *base, long long row_elems,
                                                             int row0, int n) {
-    return make_rsrc(base + row0 * row_elems, (long long)(n - row0) * row_elems * 2);
+    int rows = n - row0;
+    rows = rows < 0 ? 0 : (rows > 64 ? 64 : rows);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base + row0 * row_elems), (short)0,
+                                             rows * static_cast<int>(row_elems) * 2, 0x00020000);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -381,7 +388,7 @@ __device__ __forceinline__ bool decode_work(const Params &p, Work &w) {
 // makes them visible.
 
 template <int D, int BC, int NW, int QB, bool CAUSAL, bool VARLEN, int EXPM, int RSM, bool SPLIT = false,
-          bool MODS = false, bool COUNT = false>
+          bool MODS = false, bool COUNT = false, bool PING = false>
 __global__ void __launch_bounds__(NW * 64)
 fa_fwd_kernel(Params p) {
     using SW = Swz<D>;
@@ -394,10 +401,8 @@ fa_fwd_kernel(Params p) {
     constexpr int RB = SW::RB;
     constexpr int TB = BC * RB;          // bytes per K (or V) tile
     constexpr int BLK = TB / 1024;       // 1 KB direct-load blocks per tile
-    constexpr int BPW = BLK / NW;        // V blocks per wave per tile
     constexpr int MS = KK * NKB;         // fragment steps of one S tile (= of one PV pass)
     constexpr int NE = NKB * 16;         // S elements per lane per query block
-    static_assert(BLK % NW == 0, "tile must split evenly over waves");
     static_assert(MS == NT16 * NDB, "phase shapes");
 
     // Two K and two V tiles, as separate objects so that the compiler can see
@@ -464,19 +469,36 @@ fa_fwd_kernel(Params p) {
     // V: wave w fills 1 KB blocks w, w + NW, ...; lane l of block b fills tile
     // bytes b*1024 + 16 l = chunk slot pc of row r with logical chunk pc ^ f_V(r)
     // (f_V depends only on l).
+    // Ping-pong (PING instances, eight-wave workgroups): waves 0..3 form
+    // group 0 and waves 4..7 group 1, so every SIMD holds one wave of each.
+    // Group 1 runs half a key tile behind group 0, with a workgroup barrier
+    // every half tile: while one group issues its loads, rescales O and waits
+    // at the barrier, the other group's matrix products keep the SIMD's
+    // matrix unit busy.  Group 0 issues every K tile's loads, group 1 every V
+    // tile's.  (Measured 2-5 % slower than both groups in step: a single
+    // wave issues vector instructions too slowly to fill the matrix unit's
+    // shadow on its own, so the default keeps both waves of a SIMD
+    // interleaving products and softmax.)
+    static_assert(!PING || NW == 8, "the ping-pong pairs the two waves of a SIMD");
+    constexpr bool PP = PING;
+    constexpr int LW = PP ? NW / 2 : NW;  // waves that share one tile's loads
+    const int grp = PP ? (wave >= LW ? 1 : 0) : 0;
+    const int li = wave - grp * LW;       // this wave's index among them
     static_assert(BC == 64, "K planes are 64 rows");
-    static_assert(NW == 4 || NW == 8, "each wave's K loads must share one row parity");
-    constexpr int KLD = D / 8;           // 1 KB K loads per tile
-    constexpr int KPW = KLD / NW;        // K loads per wave
+    static_assert(LW == 4 || LW == 8, "each wave's K loads must share one row parity");
+    constexpr int KLD = D / 8;            // 1 KB K loads per tile
+    constexpr int KPW = KLD / LW;         // K loads per loading wave
+    constexpr int VPW = BLK / LW;         // V loads per loading wave
+    static_assert(KLD % LW == 0 && BLK % LW == 0, "loads must split evenly");
     const int rs_bytes = static_cast<int>(rs) * 2;
     int koff;
     {
-        const int r = 8 * (wave % 8) + lane / 8;
+        const int r = 8 * (li % 8) + lane / 8;
         koff = r * rs_bytes + (((lane % 8) ^ Swz<D>::gk(r)) << 4);
     }
     int voff;
     {
-        const int pos = wave * 1024 + lane * 16;
+        const int pos = li * 1024 + lane * 16;
         const int r = pos / RB, pc = (pos % RB) / 16;
         voff = r * rs_bytes + ((pc ^ Swz<D>::fv(r)) << 4);
     }
@@ -487,8 +509,8 @@ fa_fwd_kernel(Params p) {
         const int kv0 = (kt0 + j) * BC;
 #pragma unroll
         for (int i = 0; i < KPW; ++i) {
-            const int I = wave + NW * i;              // load index within the tile
-            const int di = (I % 8) - (wave % 8);      // rows of this load past the wave's first / 8
+            const int I = li + LW * i;                // load index within the tile
+            const int di = (I % 8) - (li % 8);        // rows of this load past the wave's first / 8
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(kg, rs, kv0 + 8 * di, n),
                                                      LDS_PTR(void, tile + I * 1024), 16, koff, (I / 8) * 128, 0, 0);
         }
@@ -497,9 +519,21 @@ fa_fwd_kernel(Params p) {
     auto dma_v = [&](char *tile, int j) {
         const int kv0 = (kt0 + j) * BC;
 #pragma unroll
-        for (int i = 0; i < BPW; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(vg, rs, kv0 + NW * i * VROWS, n),
-                                                     LDS_PTR(void, tile + (wave + NW * i) * 1024), 16, voff, 0, 0, 0);
+        for (int i = 0; i < VPW; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(vg, rs, kv0 + LW * i * VROWS, n),
+                                                     LDS_PTR(void, tile + (li + LW * i) * 1024), 16, voff, 0, 0, 0);
+    };
+    // The half-tile barrier of the ping-pong: no wait for the direct loads in
+    // flight (they are waited for before the end-of-step barrier); the empty
+    // asm keeps the compiler from moving memory accesses across it.
+    auto half_barrier = [&]() {
+        if constexpr (PP) {
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
 
     // ---- LDS fragment reads --------------------------------------------------------
@@ -832,9 +866,11 @@ fa_fwd_kernel(Params p) {
     // (a key range with no visible key for the workgroup skips straight to the
     // epilogue and stores the empty result)
     if (nkv > 0) {
-    dma_k(k_lds0, 0);
-    dma_v(v_lds0, 0);
-    if (nkv > 1) dma_k(k_lds1, 1);
+    if (!PP || grp == 0) {
+        dma_k(k_lds0, 0);
+        if (nkv > 1) dma_k(k_lds1, 1);
+    }
+    if (!PP || grp == 1) dma_v(v_lds0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (nkv_w > 0) {
@@ -848,9 +884,11 @@ fa_fwd_kernel(Params p) {
 
     // Direct loads that belong to iteration j: K_{j+2} over K_j, V_{j+1} over
     // V_{j-1} (both consumed before the previous barrier).
+    // (ping-pong: group 0 issues the K loads in its half tile, group 1 the V
+    // loads in the next; each tile then has one full step to land)
     auto issue_loads = [&](int j, char *k_dst, char *v_dst) {
-        if (j + 2 < nkv) dma_k(k_dst, j + 2);
-        if (j + 1 < nkv) dma_v(v_dst, j + 1);
+        if ((!PP || grp == 0) && j + 2 < nkv) dma_k(k_dst, j + 2);
+        if ((!PP || grp == 1) && j + 1 < nkv) dma_v(v_dst, j + 1);
     };
     auto end_iteration = [&]() {
         __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
@@ -882,6 +920,7 @@ fa_fwd_kernel(Params p) {
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (decltype(mask)::value) s_mask(nxt, j + 1);
+        half_barrier();
         float mx[QB];
         phase_b(nxt, cur, (PAR ? v_lds1 : v_lds0), mx);  // V_j
         s_update(mx);
@@ -895,6 +934,7 @@ fa_fwd_kernel(Params p) {
         tally_step(j);
         if (rescale_o) o_rescale();
         p_exp(cur);
+        half_barrier();
         pv_mfma((par ? v_lds1 : v_lds0));
         end_iteration();
     };
@@ -917,6 +957,8 @@ fa_fwd_kernel(Params p) {
     }
     const int lim = min(nkv_w, jm);
     int j = 0;
+    // ping-pong: group 1 starts half a tile behind group 0
+    if (PP && grp == 1) half_barrier();
     // leading pairs whose next tiles a window's left edge cuts
     for (; j + 1 < jh && j + 2 < nkv_w; j += 2) {
         full_step(I0{}, Mask{}, sa, sb, j);
@@ -945,8 +987,11 @@ fa_fwd_kernel(Params p) {
     // tiles past this wave's causal horizon: keep loading for the other waves
     for (; j < nkv; ++j) {
         issue_loads(j, ((j & 1) ? k_lds1 : k_lds0), ((j & 1) ? v_lds0 : v_lds1));
+        half_barrier();
         end_iteration();
     }
+    // ping-pong: group 0 waits for group 1's last half tile
+    if (PP && grp == 0) half_barrier();
     }  // nkv > 0
 
     // ---- epilogue: O / l, LSE = (m + log2 l) ln 2 ----------------------------
@@ -1040,6 +1085,16 @@ KernelFn select_count(bool causal, bool varlen, int rsm) {
                               : fa_fwd_kernel<D, BC, NW, QB, true, false, HW, TH, false, false, true>;
     return varlen ? fa_fwd_kernel<D, BC, NW, QB, false, true, HW, TH, false, false, true>
                   : fa_fwd_kernel<D, BC, NW, QB, false, false, HW, TH, false, false, true>;
+}
+
+template <int D>
+KernelFn select_ping(bool causal, bool varlen) {
+    constexpr int BC = kTileKeys, NW = Geometry<D>::kWaves, QB = Geometry<D>::kBlocks;
+    constexpr int HW = FA_EXP_HW, ST = FA_RESCALE_STRICT;
+    if (causal) return varlen ? fa_fwd_kernel<D, BC, NW, QB, true, true, HW, ST, false, false, false, true>
+                              : fa_fwd_kernel<D, BC, NW, QB, true, false, HW, ST, false, false, false, true>;
+    return varlen ? fa_fwd_kernel<D, BC, NW, QB, false, true, HW, ST, false, false, false, true>
+                  : fa_fwd_kernel<D, BC, NW, QB, false, false, HW, ST, false, false, false, true>;
 }
 
 template <int D>

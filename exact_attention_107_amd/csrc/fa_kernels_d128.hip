@@ -15,4 +15,6 @@ KernelFn select_count_d128(bool causal, bool varlen, int rescale_mode) {
     return select_count<128>(causal, varlen, rescale_mode);
 }
 
+KernelFn select_ping_d128(bool causal, bool varlen) { return select_ping<128>(causal, varlen); }
+
 }  // namespace fa_detail

@@ -22,7 +22,7 @@ RESCALE_ALWAYS, RESCALE_STRICT, RESCALE_THRESHOLD = 0, 1, 2
 EXPORTS = ("fa_fwd", "fa_fwd_variant", "fa_strerror", "fa_tile_rows", "fa_tile_keys",
            "fa_fwd_splitkv", "fa_merge", "fa_split_range", "fa_num_splits", "fa_bwd",
            "fa_bwd_workspace_floats", "fa_fwd_fp8", "fa_quantize_fp8", "fa_fp8_vt_stride",
-           "fa_fwd_masked", "fa_fwd_rescale_counts", "fa_fwd_splitkv_static")
+           "fa_fwd_masked", "fa_fwd_rescale_counts", "fa_fwd_splitkv_static", "fa_fwd_pingpong")
 FA_ERR_SCRATCH = 10
 STATIC_SCRATCH_BYTES = 64 << 20   # FA_STATIC_SCRATCH_BYTES of include/fa.h
 
@@ -80,6 +80,8 @@ def load(path: str | None = None):
     lib.fa_fp8_vt_stride.restype = i32
     lib.fa_fwd_masked.argtypes = [vp] * 5 + [i32, i32, i32, i32, ctypes.c_float, i32, i32, vp, vp]
     lib.fa_fwd_masked.restype = i32
+    lib.fa_fwd_pingpong.argtypes = common
+    lib.fa_fwd_pingpong.restype = i32
     lib.fa_fwd_rescale_counts.argtypes = common + [i32, vp]
     lib.fa_fwd_rescale_counts.restype = i32
     if path is None:
@@ -106,7 +108,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
         scale: float | None = None, cu_seqlens: torch.Tensor | None = None,
         exp_mode: int | None = None, rescale_mode: int | None = None,
         out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
-        stream: torch.cuda.Stream | None = None, counts: torch.Tensor | None = None):
+        stream: torch.cuda.Stream | None = None, counts: torch.Tensor | None = None,
+        pingpong: bool = False):
     """Exact attention forward on the GPU.
 
     q, k, v     bf16, ``[B, N, H, d]`` (dense) or ``[T, H, d]`` with
@@ -120,6 +123,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
                 instance (``fa_fwd_rescale_counts``, d = 128, hardware exp2,
                 ``rescale_mode`` strict or threshold), which adds its rescale
                 statistics to it.
+    pingpong    run ``fa_fwd_pingpong`` (d = 128; the two halves of each
+                workgroup half a key tile apart; bitwise fa_fwd's result).
     Returns ``(o, lse)``.  The kernel is queued on ``stream`` (default: the
     current stream); nothing is synchronised.
     """
@@ -169,8 +174,12 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
             raise ValueError("counts must hold 4 int64 values")
         if exp_mode not in (None, EXP_HW):
             raise ValueError("the counting instance evaluates exp2 in hardware (exp_mode EXP_HW)")
+    if pingpong and (counts is not None or exp_mode is not None or rescale_mode is not None):
+        raise ValueError("pingpong runs the default variant only (no counts, exp_mode or rescale_mode)")
     with torch.cuda.device(dev):
-        if counts is not None:
+        if pingpong:
+            rc = lib.fa_fwd_pingpong(*args)
+        elif counts is not None:
             rc = lib.fa_fwd_rescale_counts(*args, int(RESCALE_STRICT if rescale_mode is None else rescale_mode),
                                            counts.data_ptr())
         elif exp_mode is None and rescale_mode is None:

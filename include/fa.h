@@ -134,6 +134,23 @@ int fa_fwd_variant(const void *q, const void *k, const void *v, void *o,
                    int exp_mode, int rescale_mode);
 
 /*
+ * fa_fwd_pingpong: fa_fwd (hardware exp2, strict rescale) with another
+ * schedule of the same arithmetic -- the ping-pong of two query tiles of
+ * "Understanding FlashAttention V4", section 3.1: the two halves of each
+ * eight-wave workgroup (one wave of each on every SIMD, 128 query rows each)
+ * run half a key tile apart, separated by a barrier every half tile, so that
+ * one half's load issue, rescale of O and barrier wait fall under the other
+ * half's matrix products.  Head dimension 128 only (FA_ERR_HEAD_DIM for 64
+ * and 256; other values as fa_fwd).  Outputs are bitwise fa_fwd's; every
+ * other argument, the layouts and the errors are fa_fwd's.  Measured slower
+ * than fa_fwd's schedule (both halves in step, each wave interleaving its
+ * products with its softmax) on MI355X.
+ */
+int fa_fwd_pingpong(const void *q, const void *k, const void *v, void *o,
+                    float *lse, int B, int H, int N, int d, float scale,
+                    int causal, const int32_t *cu_seqlens, hipStream_t stream);
+
+/*
  * Split-KV forward (dense layout only).  For every (b, h) and query tile of
  * fa_tile_rows(d) rows, the keys that tile sees (all N, or when causal those
  * up to its last row) are cut into num_splits consecutive ranges of whole

@@ -323,3 +323,17 @@ def call_masked(lib, q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, N=100, d=128, scale=0.
 ])
 def test_masked_invalid_arguments_are_rejected(lib, kw, code):
     assert call_masked(lib, **kw) == code
+
+
+def call_ping(lib, q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, N=64, d=128, scale=0.125, causal=0, cu=None):
+    return lib.fa_fwd_pingpong(ctypes.c_void_p(q), ctypes.c_void_p(k), ctypes.c_void_p(v), ctypes.c_void_p(o),
+                               ctypes.c_void_p(lse), B, H, N, d, ctypes.c_float(scale), causal,
+                               ctypes.c_void_p(cu) if cu else None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=64), HEAD_DIM), (dict(d=256), HEAD_DIM), (dict(d=96), HEAD_DIM), (dict(q=0), NULLPTR),
+    (dict(N=0), SHAPE), (dict(scale=0.0), SCALE), (dict(o=O + 4), ALIGN), (dict(o=Q), ALIAS),
+])
+def test_pingpong_invalid_arguments_are_rejected(lib, kw, code):
+    assert call_ping(lib, **kw) == code

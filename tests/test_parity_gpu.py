@@ -195,3 +195,25 @@ def test_wide_run_variants_every_row(exp_mode, rescale_mode):
     m = every_row_parity(inp, o, lse)
     print("wide", exp_mode, rescale_mode, m)
     assert_within(m, f"wide, every row, exp_mode={exp_mode} rescale_mode={rescale_mode}")
+
+
+@pytest.mark.parametrize("name", ["mid", "mid_causal", "varlen_causal", "wide"])
+def test_pingpong_schedule_is_bitwise_the_default(name):
+    """fa_fwd_pingpong (the two halves of each workgroup half a key tile
+    apart) performs the same arithmetic in another order of issue: bitwise
+    fa_fwd's outputs on full-size runs, dense, causal and packed."""
+    inp = make_inputs(RUNS[name])
+    o1, l1 = run_gpu(inp)
+    o2, l2 = run_gpu(inp, pingpong=True)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_pingpong_ragged_and_edge(causal):
+    for N in (1, 63, 65, 300, 1000):
+        inp = _small(128, causal, N=N, B=2, H=3, seed=700 + N)
+        m, (o, lse) = full_parity(inp, pingpong=True)
+        assert_within(m, f"pingpong N={N} causal={causal}")
+        o0, l0 = run_gpu(inp)
+        assert torch.equal(o.view(torch.int16), o0.view(torch.int16)) and torch.equal(lse, l0)
