@@ -156,6 +156,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t *base
                                                             int row0, int n) {
     int rows = n - row0;
     rows = rows < 0 ? 0 : (rows > 64 ? 64 : rows);
+    // the operands are wave-uniform; say so, or the clamp may land in a
+    // vector register and every load through the resource becomes a loop
+    // over the lanes' distinct values
+    rows = __builtin_amdgcn_readfirstlane(rows);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base + row0 * row_elems), (short)0,
                                              rows * static_cast<int>(row_elems) * 2, 0x00020000);
 }
@@ -622,20 +626,33 @@ fa_fwd_kernel(Params p) {
                     }
                 continue;
             }
+            // windows: key = kv0 + 4 hh + C is visible iff lo <= C < hi, two
+            // compares per element against per-lane limits (a chain of
+            // short-circuit tests per element would compile to branches)
+            const int k0 = kv0 + 4 * hh;
+            int hi = n - k0;
+            if (CAUSAL) hi = min(hi, qrow - k0 + 1);
+            if (p.wr >= 0) hi = min(hi, qrow + p.wr - k0 + 1);
+            const int lo = p.wl >= 0 ? qrow - p.wl - k0 : -BC;
+            if (p.alibi != nullptr) {
+                // slope (j - i) on the scaled score = slope / scale on the raw one;
+                // j - i = (k0 - qrow) + C
+                const float base = static_cast<float>(k0 - qrow);
 #pragma unroll
-            for (int kb2 = 0; kb2 < NKB; ++kb2) {
+                for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int C = kb2 * 32 + (r >> 2) * 8 + (r & 3);
+                        s[b][kb2][r] = __builtin_fmaf(bias_coef, base + static_cast<float>(C), s[b][kb2][r]);
+                    }
+            }
+#pragma unroll
+            for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = kv0 + kb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-                    bool off = key >= n || (CAUSAL && key > qrow);
-                    if constexpr (MODS) {
-                        off = off || (p.wr >= 0 && key > qrow + p.wr) || (p.wl >= 0 && key < qrow - p.wl);
-                        // slope (j - i) on the scaled score = slope / scale on the raw one
-                        s[b][kb2][r] = __builtin_fmaf(bias_coef, static_cast<float>(key - qrow), s[b][kb2][r]);
-                    }
-                    s[b][kb2][r] = off ? -INFINITY : s[b][kb2][r];
+                    const int C = kb2 * 32 + (r >> 2) * 8 + (r & 3);
+                    s[b][kb2][r] = (C >= lo) & (C < hi) ? s[b][kb2][r] : -INFINITY;
                 }
-            }
         }
     };
     // Reference max update of every block from its tile's raw row max
