@@ -509,23 +509,44 @@ fa_fwd_kernel(Params p) {
     // A load whose rows start past the wave's first rows gets a resource
     // based at those rows (the size check covers the lane offset only); the
     // scalar offset carries just the plane's column offset.
+    // With eight loading waves a tile needs at most two lane offsets per
+    // tensor, so each tile gets one resource and the row offset of a load
+    // goes into its lane offset (precomputed, checked against the size);
+    // with four, a tile's loads reach up to eight row groups and each gets a
+    // resource of its own instead (scalar work, no vector registers).
+    constexpr int VROWS = 1024 / RB;     // V rows per 1 KB block
+    constexpr bool ONE_RSRC = LW == 8;
+    const int voff_hi = voff + LW * VROWS * rs_bytes;   // V loads i = 1 (eight loading waves)
     auto dma_k = [&](char *tile, int j) {
         const int kv0 = (kt0 + j) * BC;
+        const auto rsrc = rows_rsrc(kg, rs, kv0, n);
 #pragma unroll
         for (int i = 0; i < KPW; ++i) {
             const int I = li + LW * i;                // load index within the tile
             const int di = (I % 8) - (li % 8);        // rows of this load past the wave's first / 8
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(kg, rs, kv0 + 8 * di, n),
-                                                     LDS_PTR(void, tile + I * 1024), 16, koff, (I / 8) * 128, 0, 0);
+            if constexpr (ONE_RSRC)                   // di = 0: I % 8 = li % 8
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, tile + I * 1024), 16, koff,
+                                                         (I / 8) * 128, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(kg, rs, kv0 + 8 * di, n),
+                                                         LDS_PTR(void, tile + I * 1024), 16, koff, (I / 8) * 128, 0, 0);
         }
     };
-    constexpr int VROWS = 1024 / RB;     // V rows per 1 KB block
     auto dma_v = [&](char *tile, int j) {
         const int kv0 = (kt0 + j) * BC;
+        const auto rsrc = rows_rsrc(vg, rs, kv0, n);
 #pragma unroll
-        for (int i = 0; i < VPW; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(vg, rs, kv0 + LW * i * VROWS, n),
-                                                     LDS_PTR(void, tile + (li + LW * i) * 1024), 16, voff, 0, 0, 0);
+        for (int i = 0; i < VPW; ++i) {
+            if constexpr (ONE_RSRC) {
+                static_assert(!ONE_RSRC || VPW <= 2, "two V lane offsets");
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, tile + (li + LW * i) * 1024), 16,
+                                                         i == 0 ? voff : voff_hi, 0, 0, 0);
+            } else {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(vg, rs, kv0 + LW * i * VROWS, n),
+                                                         LDS_PTR(void, tile + (li + LW * i) * 1024), 16, voff, 0, 0,
+                                                         0);
+            }
+        }
     };
     // The half-tile barrier of the ping-pong: no wait for the direct loads in
     // flight (they are waited for before the end-of-step barrier); the empty
@@ -801,17 +822,23 @@ fa_fwd_kernel(Params p) {
     float rsum_a[QB];
 
     // [A]: S_{j+1} MFMAs interleaved with the first half of the exponentials of S_j.
-    auto phase_a = [&](f32x16 (&nxt)[QB][NKB], const f32x16 (&cur)[QB][NKB], const char *kb) {
+    // The first KLA K fragments are read by the caller (k_prefetch) at the
+    // top of the step, so that their LDS latency passes under the load issue
+    // and the O rescale instead of stalling the first MFMA.
+    constexpr int KLA = kKLookahead < MS ? kKLookahead : MS;  // fragments in flight
+    auto k_prefetch = [&](bf16x8 (&kf)[KLA + 1], const char *kb) {
+        // step order alternates the NKB accumulator chains
+        static_for<0, KLA>([&](auto i) { kf[i] = kfrag(kb, i / NKB, i % NKB); });
+    };
+    auto phase_a = [&](f32x16 (&nxt)[QB][NKB], const f32x16 (&cur)[QB][NKB], const char *kb,
+                       bf16x8 (&kf)[KLA + 1]) {
 #pragma unroll
         for (int b = 0; b < QB; ++b) {
             rsum_a[b] = 0.0f;
 #pragma unroll
             for (int i = 0; i < NKB; ++i) nxt[b][i] = f32x16{};
         }
-        constexpr int LA = kKLookahead < MS ? kKLookahead : MS;  // fragments in flight
-        bf16x8 kf[LA + 1];
-        // step order alternates the NKB accumulator chains
-        static_for<0, LA>([&](auto i) { kf[i] = kfrag(kb, i / NKB, i % NKB); });
+        constexpr int LA = KLA;
         static_for<0, MS>([&](auto m) {
             constexpr int kb2 = m % NKB, kk = m / NKB;
             if constexpr (m + LA < MS) kf[(m + LA) % (LA + 1)] = kfrag(kb, (m + LA) / NKB, (m + LA) % NKB);
@@ -829,7 +856,6 @@ fa_fwd_kernel(Params p) {
         });
 #pragma unroll
         for (int b = 0; b < QB; ++b) anchor(rsum_a[b]);
-        __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);  // first K fragments
         static_for<0, MS>([&](auto m) {
             constexpr int ne = (m + 1) * AE / MS - m * AE / MS;  // elements of this step
             __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);  // MFMA
@@ -926,6 +952,8 @@ fa_fwd_kernel(Params p) {
     };
     auto full_step = [&](auto par, auto mask, f32x16 (&cur)[QB][NKB], f32x16 (&nxt)[QB][NKB], int j) {
         constexpr int PAR = decltype(par)::value;
+        bf16x8 kf[KLA + 1];
+        k_prefetch(kf, (PAR ? k_lds0 : k_lds1));  // K_{j+1}, in LDS since the last barrier
         issue_loads(j, (PAR ? k_lds1 : k_lds0), (PAR ? v_lds0 : v_lds1));
         tally_step(j);
         if (rescale_o) o_rescale();
@@ -933,7 +961,7 @@ fa_fwd_kernel(Params p) {
         // the score MFMAs go first when the SIMD's two waves compete for
         // issue (measured +1 %)
         __builtin_amdgcn_s_setprio(1);
-        phase_a(nxt, cur, (PAR ? k_lds0 : k_lds1));  // K_{j+1}
+        phase_a(nxt, cur, (PAR ? k_lds0 : k_lds1), kf);  // K_{j+1}
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (decltype(mask)::value) s_mask(nxt, j + 1);
