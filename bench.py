@@ -517,13 +517,14 @@ def main() -> int:
             rl_shape = (ri["H"], ri["T"]) if rcu is not None else (ri["B"], ri["H"], ri["N"])
             rl = torch.empty(rl_shape, dtype=torch.float32, device="cuda")
             rf = flops(ri["lengths"], ri["H"], ri["d"], ri["causal"])
-            res = {}
-            for sched, pp in (("in_step", False), ("pingpong", True)):
-                def plaunch():
-                    fa.fwd(rq, rk, rv, causal=ri["causal"], scale=ri["scale"], cu_seqlens=rcu, out=ro, lse=rl,
-                           pingpong=pp)
-                _, kms, _, _ = time_launches(plaunch, 30, 20, torch)
-                res[sched] = round(rf / (kms * 1e-3) / 1e12, 1)
+            res = {"in_step": 0.0, "pingpong": 0.0}
+            for _ in range(3):  # alternate the two schedules; best of three each
+                for sched, pp in (("in_step", False), ("pingpong", True)):
+                    def plaunch():
+                        fa.fwd(rq, rk, rv, causal=ri["causal"], scale=ri["scale"], cu_seqlens=rcu, out=ro, lse=rl,
+                               pingpong=pp)
+                    _, kms, _, _ = time_launches(plaunch, 30, 20, torch)
+                    res[sched] = max(res[sched], round(rf / (kms * 1e-3) / 1e12, 1))
             pingpong[name] = res
             del rq, rk, rv, ro, rl
         out["pingpong_tflops"] = pingpong

@@ -24,13 +24,16 @@ COMMON = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 # Keep MFMA accumulators in architectural VGPRs, where the softmax rescale and
-# the epilogue operate on them in place.  Not for d = 256, whose accumulators
-# do not fit beside the other operands and take the accumulation registers.
+# the epilogue operate on them in place.  At d = 256 (one wave per SIMD) the
+# values that do not fit then spill into the accumulation registers instead
+# of scratch; with the accumulators there instead, every score tile and every
+# rescale of O went through accvgpr moves (~900 per key tile; measured 15 %
+# slower).
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 UNITS = [
     ("fa_kernels_d64.hip", VGPR_FORM),
     ("fa_kernels_d128.hip", VGPR_FORM),
-    ("fa_kernels_d256.hip", []),
+    ("fa_kernels_d256.hip", VGPR_FORM),
     ("fa_bwd_d64.hip", VGPR_FORM),
     ("fa_bwd_d128.hip", VGPR_FORM),
     ("fa_fp8.hip", []),
