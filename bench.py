@@ -321,6 +321,57 @@ def masked_runs(torch, fa):
     return res
 
 
+def other_pass(torch, fa, which, workload, steps, warmup, settle_s=0.0):
+    """One kernel family alone on one workload, for profiling: the FP8
+    forward (inputs quantised once, outside the timed launches), the split-KV
+    forward with the library's split count (split kernel and merge in each
+    launch), or the masked forward's sliding window with ALiBi."""
+    from exact_attention_107_amd.workloads import Run, RUNS, flops, make_inputs
+    if which == "masked":
+        r = Run("masked", 1, 16, 16384, 128, False, 1009)
+    else:
+        r = RUNS[workload]
+    ri = make_inputs(r)
+    q, k, v = (to_dev(ri[x], torch) for x in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty((r.B, r.H, r.N), dtype=torch.float32, device="cuda")
+    f = flops(ri["lengths"], r.H, r.d, r.causal)
+    label = f"{r.name}: B={r.B} H={r.H} N={r.N} d={r.d} causal={r.causal}"
+    res = {}
+    if which == "fp8":
+        q8, dq = fa.quantize_fp8(q)
+        k8, dk = fa.quantize_fp8(k)
+        vt8, dv = fa.quantize_fp8(v, transpose=True)
+
+        def launch():
+            fa.fwd_fp8(q8, k8, vt8, dq, dk, dv, causal=r.causal, scale=ri["scale"], out=o, lse=lse)
+    elif which == "split":
+        S = fa.num_splits(r.B, r.H, r.N, r.d, r.causal, torch.cuda.get_device_properties(0).multi_processor_count)
+        op = torch.empty((S, r.B, r.N, r.H, r.d), dtype=torch.float32, device="cuda")
+        lp = torch.empty((S, r.B, r.H, r.N), dtype=torch.float32, device="cuda")
+        res["splits"] = S
+
+        def launch():
+            fa.fwd_splitkv(q, k, v, causal=r.causal, scale=ri["scale"], splits=S, out=o, lse=lse, o_part=op,
+                           lse_part=lp)
+    else:
+        W = 1024
+        slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / r.H) for h in range(r.H)], dtype=torch.float32,
+                              device="cuda")
+        f = 4.0 * r.d * r.H * r.B * sum(min(i + 1, W + 1) for i in range(r.N))
+        label += f", window of {W} keys to the left, causal, ALiBi slopes 2^(-8(h+1)/H)"
+
+        def launch():
+            fa.fwd_masked(q, k, v, scale=ri["scale"], out=o, lse=lse, window_left=W, window_right=0,
+                          alibi_slopes=slopes)
+    log(f"[bench] {which} pass on {label}")
+    if settle_s > 0:
+        res["clock_settle_launches"] = settle_clock(launch, settle_s, torch)
+    ms_step, ms, _, _ = time_launches(launch, steps, warmup, torch)
+    res.update({"ms": round(ms, 5), "tflops": round(f / ms / 1e9, 1)})
+    return res, f, ms_step, ms, label
+
+
 def rescale_rates(torch, fa):
     """How often the conditional rescale fires (counting instance of the
     kernel, one launch per run and rule): the share of wave-steps (64 keys x 32
@@ -381,8 +432,10 @@ def main() -> int:
     ap.add_argument("--extra", type=int, default=1, help="also time the other runs and variants")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
-                    help="bwd: time only the backward pass of --workload (for profiling)")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "fp8", "split", "masked"), default="fwd",
+                    help="time only one other kernel family on --workload (for profiling): bwd = the "
+                         "backward pass, fp8 = the FP8 forward, split = the split-KV forward and merge, "
+                         "masked = the 1024-key sliding window with ALiBi (fixed shape)")
     ap.add_argument("--settle-s", type=float, default=0.5,
                     help="seconds of untimed launches before the warmup, so that the timed steps "
                          "run at the clock the GPU holds under this load (0: none)")
@@ -414,6 +467,17 @@ def main() -> int:
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": f"{args.workload}: {res['shape']}"}, "roofline": res["roofline"],
             "kernel_fingerprint": kernel_fingerprint()}), flush=True)
+        return 0
+    if args.which in ("fp8", "split", "masked"):
+        res, f, ms_step, ms_kernel, label = other_pass(torch, fa, args.which, args.workload, args.steps,
+                                                       args.warmup, args.settle_s)
+        print(json.dumps({
+            "metric": f"attention {args.which} forward TFLOP/s (credited 4*B*H*N^2*d, halved causal)",
+            "value": round(f / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "fp8-e4m3" if args.which == "fp8" else "bf16", "data": "synthetic",
+            "config": {"workload": label}, "result": res, "kernel_fingerprint": kernel_fingerprint()}), flush=True)
         return 0
     run = RUNS[args.workload]
     log(f"[bench] generating {run.name} inputs")
