@@ -594,7 +594,8 @@ def main() -> int:
         out["pingpong_tflops"] = pingpong
         out["split_kv"] = split_kv_runs(torch, fa)
         out["backward"] = {name: backward_run(torch, fa, name)[0]
-                           for name in ("mid", "mid_causal", "bwd_long", "bwd_long_causal", "varlen_causal")}
+                           for name in ("mid", "mid_causal", "bwd_long", "bwd_long_causal", "varlen_causal",
+                                        "wide_d256")}
         out["fp8"] = fp8_runs(torch, fa)
         out["masked"] = masked_runs(torch, fa)
         out["rescale_rates"] = rescale_rates(torch, fa)

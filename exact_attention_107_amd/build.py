@@ -36,6 +36,10 @@ UNITS = [
     ("fa_kernels_d256.hip", VGPR_FORM),
     ("fa_bwd_d64.hip", VGPR_FORM),
     ("fa_bwd_d128.hip", VGPR_FORM),
+    # d = 256 backward, one wave per SIMD: the 256 dK/dV accumulator values
+    # live in the accumulation registers, which the MFMAs read and write in
+    # place (neither form spills to scratch)
+    ("fa_bwd_d256.hip", []),
     ("fa_fp8.hip", []),
     ("fa_merge.hip", []),
     ("fa_api.hip", []),

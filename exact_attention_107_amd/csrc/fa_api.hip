@@ -338,7 +338,7 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const flo
            const int32_t *cu_seqlens, float *workspace, hipStream_t stream) {
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return FA_ERR_NULLPTR;
     if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
-    if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+    if (d != 64 && d != 128 && d != 256) return FA_ERR_HEAD_DIM;
     if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_SCALE;
     const void *t16[] = {q, k, v, o, dout, dq, dk, dv, workspace};
     for (const void *t : t16)
@@ -379,7 +379,9 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const flo
     bp.N = N;
     bp.cs = scale * kLog2e;
     bp.scale = scale;
-    const BwdKernels ks = d == 64 ? select_bwd_d64(causal != 0, packed) : select_bwd_d128(causal != 0, packed);
+    const BwdKernels ks = d == 64    ? select_bwd_d64(causal != 0, packed)
+                          : d == 128 ? select_bwd_d128(causal != 0, packed)
+                                     : select_bwd_d256(causal != 0, packed);
     // key tiles of the dK/dV kernel and query tiles of the dQ kernel: 128
     // each; packed: a bound on sum_b ceil(n_b / 128), surplus workgroups exit
     const long long tiles = (static_cast<long long>(N) + 127) / 128;

@@ -65,30 +65,41 @@ template <int D> struct BwdTile {
 // Direct global->LDS loads of ROWS rows into a BwdTile: 1 KB per load, the
 // workgroup's NW waves take loads wave, wave + NW, ...  Lane l of load I
 // fills row r = (1024 I + 16 l) / RB, physical chunk pc, with logical chunk
-// pc ^ sg(r); sg depends on r mod 16 only, which is the same for all of a
-// wave's loads, so one per-lane offset serves them all.
+// pc ^ sg(r); sg depends on r mod 16 only.  A wave's loads are NW * RPB rows
+// apart: for D <= 128 a multiple of 16, so one per-lane offset serves them
+// all; for D = 256 (two rows per load, eight rows apart) loads of even and
+// odd index take two offsets.
 template <int D, int ROWS, int NW> struct BwdDma {
     static constexpr int RB = D * 2;
     static constexpr int BLK = ROWS * RB / 1024;
     static constexpr int PER = BLK / NW;
     static constexpr int RPB = 1024 / RB;  // rows per load
+    static constexpr int NV = (NW * RPB) % 16 == 0 ? 1 : 2;  // lane offsets per wave
     static_assert(BLK % NW == 0, "tile must split evenly over the waves");
-    static_assert((NW * RPB) % 16 == 0, "a wave's loads must share sg");
-    static __device__ __forceinline__ int voff(int wave, int lane, int rs_bytes) {
+    static_assert((NV * NW * RPB) % 16 == 0, "a wave's loads must take at most two swizzles");
+    struct Off {
+        int v[NV];
+    };
+    static __device__ __forceinline__ Off voff(int wave, int lane, int rs_bytes) {
         const int pos = wave * 1024 + lane * 16;
         const int r = pos / RB, pc = (pos % RB) / 16;
-        return r * rs_bytes + ((pc ^ BwdTile<D>::sg(r)) << 4);
+        Off o;
+#pragma unroll
+        for (int i = 0; i < NV; ++i)   // the row offset is the first load's; the swizzle load i's
+            o.v[i] = r * rs_bytes + ((pc ^ BwdTile<D>::sg(r + NW * i * RPB)) << 4);
+        return o;
     }
     // Rows row0 .. row0 + ROWS - 1 of the tensor at g (row stride rs
     // elements); rows at or past n read as zeros.  Load i covers rows
     // NW i RPB .. further on than the lane offset says, so it gets a resource
     // based at those rows: the size check covers the lane offset only.
     static __device__ __forceinline__ void load(const uint16_t *g, long long rs, int row0, int n, char *tile,
-                                                int wave, int voff) {
+                                                int wave, const Off &vo) {
 #pragma unroll
         for (int i = 0; i < PER; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(g, rs, row0 + NW * i * RPB, n),
-                                                     LDS_PTR(void, tile + (wave + NW * i) * 1024), 16, voff, 0, 0, 0);
+                                                     LDS_PTR(void, tile + (wave + NW * i) * 1024), 16,
+                                                     vo.v[i % NV], 0, 0, 0);
     }
 };
 
@@ -260,7 +271,7 @@ __device__ __forceinline__ bool bwd_packed_item(const BwdParams &p, BwdItem &it)
 // dK, dV: workgroup = (b, h, key tile of 128 keys).
 
 template <int D, bool CAUSAL, bool PACKED>
-__global__ void __launch_bounds__(kBwdWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(kBwdWaves * 64) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
 fa_bwd_dkdv_kernel(BwdParams p) {
     constexpr int NW = kBwdWaves, KW = kBwdKeysPerWave, BK = kBwdKeyTile, BQ = kBwdQBlock;
     constexpr int KK = D / 16, NDB = D / 32, RB = D * 2;
@@ -324,8 +335,8 @@ fa_bwd_dkdv_kernel(BwdParams p) {
 
     BwdAddr<D> ad;
     ad.init(lane);
-    const int qvoff = QDMA::voff(wave, lane, rs_bytes);
-    const int vvoff = VDMA::voff(wave, lane, rs_bytes);
+    const auto qvoff = QDMA::voff(wave, lane, rs_bytes);
+    const auto vvoff = VDMA::voff(wave, lane, rs_bytes);
     // (LSE*log2e, delta) pairs of the sequence's rows; lane l < 32 fetches
     // row l's LSE, lane 32 + l its delta: st_lds = [32 x LSE*log2e | 32 x delta]
     const float *stats_seq = p.stats + 2 * it.lrow;
@@ -455,7 +466,10 @@ fa_bwd_dkdv_kernel(BwdParams p) {
         if (qb + 1 < nqb) dma_block(qb + 1, PAR ? q_lds0 : q_lds1, PAR ? do_lds0 : do_lds1, PAR ? st_lds0 : st_lds1);
         const int q0 = qb * BQ;
         // causal: queries q0 .. q0+31 all precede this wave's keys -> nothing
-        if (!CAUSAL || q0 + BQ - 1 >= kw0) {
+        // to add (for D = 256 the block runs anyway, fully masked: the first
+        // `wave` blocks of waves 1..3; branching round it makes the compiler
+        // spill the 256 accumulator registers)
+        if (!CAUSAL || D == 256 || q0 + BQ - 1 >= kw0) {
             block(qcur, dcur, scur, q0, key_tail || q0 + BQ > n || (CAUSAL && q0 < kw0 + KW));
         }
         __builtin_amdgcn_s_waitcnt(0);
@@ -493,7 +507,7 @@ fa_bwd_dkdv_kernel(BwdParams p) {
 // dQ: workgroup = (b, h, query tile of 128 rows), like the forward.
 
 template <int D, bool CAUSAL, bool PACKED>
-__global__ void __launch_bounds__(kBwdWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(kBwdWaves * 64) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
 fa_bwd_dq_kernel(BwdParams p) {
     constexpr int NW = kBwdWaves, BR = kBwdQTile, BC = kBwdKvTile;
     constexpr int KK = D / 16, NDB = D / 32, RB = D * 2, NKB = BC / 32;
@@ -558,7 +572,7 @@ fa_bwd_dq_kernel(BwdParams p) {
 
     BwdAddr<D> ad;
     ad.init(lane);
-    const int kvoff = KDMA::voff(wave, lane, rs_bytes);
+    const auto kvoff = KDMA::voff(wave, lane, rs_bytes);
     const int kv_end = CAUSAL ? min(n, q0 + BR) : n;
     const int nkv = (kv_end + BC - 1) / BC;
     const int nkv_w = CAUSAL ? min(nkv, (wrow0 + 31) / BC + 1) : nkv;

@@ -121,6 +121,7 @@ struct BwdKernels {
 };
 BwdKernels select_bwd_d64(bool causal, bool packed);
 BwdKernels select_bwd_d128(bool causal, bool packed);
+BwdKernels select_bwd_d256(bool causal, bool packed);
 
 // FP8 (E4M3) forward and quantisation (fa_fp8_kernel.hpp).
 struct Fp8Params {

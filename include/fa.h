@@ -242,7 +242,7 @@ int fa_split_range(int N, int d, int causal, int num_splits, int s, int row,
 int fa_num_splits(int B, int H, int N, int d, int causal, int num_cus);
 
 /*
- * fa_bwd: gradients of exact attention (d = 64 or 128), dense or packed.
+ * fa_bwd: gradients of exact attention (d = 64, 128 or 256), dense or packed.
  * For the forward O = softmax(scale Q K^T) V and an upstream gradient dO it
  * writes
  *     dV = P^T dO,  dQ = scale dS K,  dK = scale dS^T Q,
@@ -266,8 +266,7 @@ int fa_num_splits(int B, int H, int N, int d, int causal, int num_cus);
  *                     aligned); overwritten.
  *   B, H, N, scale, causal, stream   as fa_fwd.
  * Three kernels are queued on `stream`.  Outputs and the workspace must not
- * overlap any input or each other.  Errors as fa_fwd; FA_ERR_HEAD_DIM for
- * d = 256, which the backward does not support.
+ * overlap any input or each other.  Errors as fa_fwd.
  */
 int fa_bwd(const void *q, const void *k, const void *v, const void *o,
            const float *lse, const void *dout, void *dq, void *dk, void *dv,

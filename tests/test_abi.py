@@ -266,7 +266,7 @@ def call_bwd(lib, q=Q, k=K, v=V, o=O, lse=L, do=DO, dq=DQ, dk=DK, dv=DV, B=1, H=
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=0), NULLPTR), (dict(do=0), NULLPTR), (dict(dv=0), NULLPTR), (dict(ws=0), NULLPTR),
-    (dict(N=0), SHAPE), (dict(H=(1 << 22) // 128 + 1), SHAPE), (dict(d=256), HEAD_DIM), (dict(d=32), HEAD_DIM),
+    (dict(N=0), SHAPE), (dict(H=(1 << 22) // 128 + 1), SHAPE), (dict(d=96), HEAD_DIM), (dict(d=32), HEAD_DIM),
     (dict(scale=0.0), SCALE), (dict(dq=DQ + 8), ALIGN), (dict(ws=WS + 4), ALIGN), (dict(lse=L + 2), ALIGN),
     (dict(dq=Q), ALIAS), (dict(dk=DO + 64), ALIAS), (dict(dv=DQ), ALIAS), (dict(ws=L), ALIAS),
     (dict(ws=DK + 128), ALIAS), (dict(cu=0x80000002), ALIGN),

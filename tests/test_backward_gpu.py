@@ -70,7 +70,7 @@ def _oracle(inp):
                               causal=inp["causal"])
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_small_ragged(d, causal):
     """Several key tiles and query blocks with ragged tails, every element."""
@@ -106,14 +106,23 @@ def test_bwd_deterministic():
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
-def test_bwd_rejects_d256():
-    q = torch.zeros(1, 64, 1, 256, dtype=torch.bfloat16, device="cuda")
+@pytest.mark.parametrize("N", [1, 33, 129, 160, 390])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_d256_edge_lengths(N, causal):
+    """d = 256 (two rows per direct load, one wave per SIMD; causal blocks
+    above the diagonal run fully masked instead of being skipped)."""
+    inp = _inputs(256, causal, N, B=1, H=2, seed=400 + N)
+    _check(_gpu(inp), _oracle(inp), f"d=256 N={N} causal={causal}")
+
+
+def test_bwd_rejects_other_head_dims():
+    q = torch.zeros(1, 64, 1, 96, dtype=torch.bfloat16, device="cuda")
     lse = torch.zeros(1, 1, 64, dtype=torch.float32, device="cuda")
     with pytest.raises(fa.FaError):
         fa.bwd(q, q.clone(), q.clone(), q.clone(), lse, q.clone())
 
 
-@pytest.mark.parametrize("name", ["mid", "mid_causal"])
+@pytest.mark.parametrize("name", ["mid", "mid_causal", "wide_d256"])
 def test_bwd_full_size_sampled_heads(name):
     """The benchmark's backward shapes at full size; two (b, h) heads are
     checked in full (each head's gradients depend on that head alone)."""
@@ -153,7 +162,7 @@ def _oracle_packed(inp):
                               causal=inp["causal"], cu_seqlens=inp["cu_seqlens"])
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_packed_small(d, causal):
     """Empty, one-token and ragged sequences in one packed batch, every element."""
