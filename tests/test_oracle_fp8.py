@@ -145,3 +145,103 @@ def test_quantize_step_order_pinned_by_hand_derived_codes():
         assert int(codes[0, 0, 0, 1]) == c["code"], c
         assert int(codes[0, 0, 0, 1]) != c["code_alternative"]
         assert int(codes[0, 0, 0, 0]) == 0x7E          # amax itself maps to 448
+
+
+# ---------------------------------------------------------------------------
+# Packed sequences: per-sequence reductions to the dense functions pinned above.
+
+PACKED_LENGTHS = [5, 0, 64, 1, 65, 130, 0, 37]
+
+
+def _packed_x(seed, H=3, d=16, scales=(1.0, 10.0, 0.1)):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    T = sum(PACKED_LENGTHS)
+    x = bf16_bits((rng.standard_normal((T, H, d)) * np.array(scales)[None, :, None]).astype(np.float32))
+    cu = np.concatenate([[0], np.cumsum(PACKED_LENGTHS)]).astype(np.int32)
+    # one sequence with an all-zero head (descale 1, zero codes)
+    x[cu[3]:cu[4], 1, :] = 0
+    return x, cu
+
+
+def test_quantize_packed_equals_per_sequence_quantize():
+    x, cu = _packed_x(21)
+    T, H, d = x.shape
+    B = len(PACKED_LENGTHS)
+    codes, ds = fp8.quantize_packed(x, cu)
+    vt, dst = fp8.quantize_packed(x, cu, transpose=True)
+    assert codes.shape == (T, H, d) and ds.shape == (B, H) and np.array_equal(ds, dst)
+    Tp = (T + 63) // 64 * 64 + 64 * B
+    assert vt.shape == (H, d, Tp)
+    start = 0                                   # padded start, accumulated here
+    covered = np.zeros(Tp, dtype=bool)
+    for b, n in enumerate(PACKED_LENGTHS):
+        t0 = int(cu[b])
+        if n == 0:
+            assert np.all(ds[b] == 1.0)
+            continue
+        c1, d1 = fp8.quantize(x[None, t0:t0 + n])
+        assert np.array_equal(codes[t0:t0 + n], c1[0]) and np.array_equal(ds[b], d1[0])
+        pad = (n + 63) // 64 * 64
+        assert np.array_equal(vt[:, :, start:start + n], c1[0].transpose(1, 2, 0))
+        assert np.all(vt[:, :, start + n:start + pad] == 0)
+        covered[start:start + pad] = True
+        start += pad
+    assert np.all(vt[:, :, ~covered] == 0)
+    assert np.all(ds[3, 1] == 1.0) and np.all(codes[cu[3]:cu[4], 1] == 0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_packed_equals_per_sequence_dense(causal):
+    q, cu = _packed_x(22, H=2, d=16, scales=(1.0, 2.0))
+    k, _ = _packed_x(23, H=2, d=16, scales=(1.0, 2.0))
+    v, _ = _packed_x(24, H=2, d=16, scales=(1.0, 2.0))
+    q8, dq = fp8.quantize_packed(q, cu)
+    k8, dk = fp8.quantize_packed(k, cu)
+    vt8, dv = fp8.quantize_packed(v, cu, transpose=True)
+    o, lse = fp8.attention_packed(q8, k8, vt8, dq, dk, dv, cu, scale=0.3, causal=causal)
+    rows = []
+    for b, n in enumerate(PACKED_LENGTHS):
+        if n == 0:
+            continue
+        t0 = int(cu[b])
+        sl = lambda a: a[None, t0:t0 + n]
+        c_v, d_v = fp8.quantize(sl(v), transpose=True)
+        ro, rl = fp8.attention(sl(q8), sl(k8), c_v, dq[b:b + 1], dk[b:b + 1], d_v, scale=0.3, causal=causal)
+        assert np.array_equal(d_v, dv[b:b + 1])
+        assert np.max(np.abs(o[t0:t0 + n] - ro[0])) <= 1e-12 * max(1.0, np.abs(ro).max())
+        assert np.max(np.abs(lse[:, t0:t0 + n] - rl[0])) <= 1e-10
+        rows += [[b, 0, 0], [b, 1, n - 1]]
+    rows = np.array(rows)
+    orow, lrow = fp8.attention_packed(q8, k8, vt8, dq, dk, dv, cu, scale=0.3, causal=causal, rows=rows)
+    tok = cu[rows[:, 0]] + rows[:, 2]
+    assert np.allclose(orow, o[tok, rows[:, 1]], rtol=0, atol=1e-12)
+    assert np.allclose(lrow, lse[rows[:, 1], tok], rtol=0, atol=1e-12)
+
+
+def test_packed_planted_mistakes_are_caught(monkeypatch):
+    """Broken copies of the packed helpers fail the two tests above."""
+    good_starts = fp8.padded_starts
+    monkeypatch.setattr(fp8, "padded_starts", lambda cu: np.asarray(cu[:-1], np.int64))  # no padding
+    with pytest.raises(AssertionError):
+        test_quantize_packed_equals_per_sequence_quantize()
+    monkeypatch.setattr(fp8, "padded_starts", good_starts)
+    good_q = fp8.quantize_packed
+
+    def global_amax(x_bits, cu, transpose=False):      # one scale per head over all sequences
+        x = np.asarray(x_bits)
+        c, d = good_q(x, np.array([0, x.shape[0]], np.int32), transpose=False)
+        if transpose:
+            return good_q(x, cu, transpose=True)
+        return c, np.repeat(d, len(cu) - 1, axis=0)
+    monkeypatch.setattr(fp8, "quantize_packed", global_amax)
+    with pytest.raises(AssertionError):
+        test_quantize_packed_equals_per_sequence_quantize()
+    monkeypatch.setattr(fp8, "quantize_packed", good_q)
+    good_att = fp8.attention_packed
+
+    def whole_batch(q8, k8, vt8, dq, dk, dv, cu, **kw):  # sequences see each other's keys
+        T = q8.shape[0]
+        return good_att(q8, k8, vt8, dq[:1], dk[:1], dv[:1], np.array([0, T]), **kw)
+    monkeypatch.setattr(fp8, "attention_packed", whole_batch)
+    with pytest.raises((AssertionError, ValueError, IndexError)):
+        test_attention_packed_equals_per_sequence_dense(True)
