@@ -40,7 +40,10 @@ UNITS = [
     # live in the accumulation registers, which the MFMAs read and write in
     # place (neither form spills to scratch)
     ("fa_bwd_d256.hip", []),
-    ("fa_fp8.hip", []),
+    # FP8: d = 64 and 128 allocate the same either way; at d = 256 (one wave
+    # per SIMD) the VGPR form keeps the O accumulators where the rescale and
+    # the epilogue use them
+    ("fa_fp8.hip", VGPR_FORM),
     ("fa_merge.hip", []),
     ("fa_api.hip", []),
 ]

@@ -449,46 +449,87 @@ int fa_fwd_masked(const void *q, const void *k, const void *v, void *o, float *l
 
 int fa_fp8_vt_stride(int N) { return N < 1 ? 0 : (N + 63) / 64 * 64; }
 
-int fa_quantize_fp8(const void *x, void *x8, float *descale, int B, int H, int N, int d, int transpose,
-                    hipStream_t stream) {
+int fa_fp8_vt_stride_packed(int T, int B) {
+    if (T < 1 || B < 1) return 0;
+    const long long s = (static_cast<long long>(T) + 63) / 64 * 64 + 64LL * B;
+    return s > 0x7fffffffLL ? 0 : static_cast<int>(s);
+}
+
+// Quantisation, dense (cu_seqlens == nullptr: x [B, N, H, d]) or packed
+// (x [T, H, d], N = T, B sequences).
+static int quant_impl(const void *x, void *x8, float *descale, const int32_t *cu_seqlens, int B, int H, int N,
+                      int d, int transpose, hipStream_t stream) {
     if (!x || !x8 || !descale) return FA_ERR_NULLPTR;
     if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
     if (d != 64 && d != 128 && d != 256) return FA_ERR_HEAD_DIM;
-    if (misaligned(x, 16) || misaligned(x8, 4) || misaligned(descale, 4)) return FA_ERR_ALIGN;
-    const long long tokens = transpose ? fa_fp8_vt_stride(N) : N;
-    const long long elems = static_cast<long long>(B) * H * tokens * d;
-    if (elems <= 0 || elems > (1LL << 46) || !token_stride_ok(H, d)) return FA_ERR_SHAPE;
-    const size_t xb = static_cast<size_t>(B) * N * H * d * 2, x8b = static_cast<size_t>(elems);
-    const size_t db = static_cast<size_t>(B) * H * 4;
-    if (overlap(x8, x8b, x, xb) || overlap(descale, db, x, xb) || overlap(descale, db, x8, x8b)) return FA_ERR_ALIAS;
+    if (misaligned(x, 16) || misaligned(x8, 4) || misaligned(descale, 4) || misaligned(cu_seqlens, 4))
+        return FA_ERR_ALIGN;
+    const bool packed = cu_seqlens != nullptr;
+    const long long rows = packed ? static_cast<long long>(N) * H : static_cast<long long>(B) * N * H;
+    long long x8_elems;
+    if (!transpose) {
+        x8_elems = rows * d;
+    } else if (packed) {
+        const int vts = fa_fp8_vt_stride_packed(N, B);
+        if (vts == 0 || static_cast<long long>(d) * vts > 0x7fffffffLL) return FA_ERR_SHAPE;
+        x8_elems = static_cast<long long>(H) * d * vts;
+    } else {
+        x8_elems = static_cast<long long>(B) * H * d * fa_fp8_vt_stride(N);
+    }
+    if (rows * d <= 0 || rows * d > (1LL << 46) || x8_elems > (1LL << 46) || !token_stride_ok(H, d))
+        return FA_ERR_SHAPE;
+    const size_t xb = static_cast<size_t>(rows) * d * 2, x8b = static_cast<size_t>(x8_elems);
+    const size_t db = static_cast<size_t>(B) * H * 4, cb = packed ? static_cast<size_t>(B + 1) * 4 : 0;
+    if (overlap(x8, x8b, x, xb) || overlap(descale, db, x, xb) || overlap(descale, db, x8, x8b) ||
+        (packed && (overlap(x8, x8b, cu_seqlens, cb) || overlap(descale, db, cu_seqlens, cb))))
+        return FA_ERR_ALIAS;
     QuantParams qp;
     qp.x = static_cast<const uint16_t *>(x);
     qp.x8 = static_cast<uint8_t *>(x8);
     qp.descale = descale;
+    qp.cu = cu_seqlens;
     qp.B = B;
     qp.H = H;
     qp.N = N;
     qp.d = d;
     qp.transpose = transpose != 0;
+    qp.vts = packed ? fa_fp8_vt_stride_packed(N, B) : 0;
     (void)hipGetLastError();
     return launch_quant(qp, stream) == 0 ? FA_OK : FA_ERR_HIP;
 }
 
-int fa_fwd_fp8(const void *q8, const void *k8, const void *vt8, const float *descale_q, const float *descale_k,
-               const float *descale_v, void *o, float *lse, int B, int H, int N, int d, float scale, int causal,
-               hipStream_t stream) {
+int fa_quantize_fp8(const void *x, void *x8, float *descale, int B, int H, int N, int d, int transpose,
+                    hipStream_t stream) {
+    return quant_impl(x, x8, descale, nullptr, B, H, N, d, transpose, stream);
+}
+
+int fa_quantize_fp8_packed(const void *x, void *x8, float *descale, const int32_t *cu_seqlens, int B, int H,
+                           int T, int d, int transpose, hipStream_t stream) {
+    if (!cu_seqlens) return FA_ERR_NULLPTR;
+    return quant_impl(x, x8, descale, cu_seqlens, B, H, T, d, transpose, stream);
+}
+
+// FP8 forward, dense or packed (as quant_impl).
+static int fwd_fp8_impl(const void *q8, const void *k8, const void *vt8, const float *descale_q,
+                        const float *descale_k, const float *descale_v, void *o, float *lse,
+                        const int32_t *cu_seqlens, int B, int H, int N, int d, float scale, int causal,
+                        hipStream_t stream) {
     if (!q8 || !k8 || !vt8 || !descale_q || !descale_k || !descale_v || !o || !lse) return FA_ERR_NULLPTR;
     if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
-    if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+    if (d != 64 && d != 128 && d != 256) return FA_ERR_HEAD_DIM;
     if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_SCALE;
     if (misaligned(q8, 16) || misaligned(k8, 16) || misaligned(vt8, 16) || misaligned(o, 16) ||
-        misaligned(lse, 4) || misaligned(descale_q, 4) || misaligned(descale_k, 4) || misaligned(descale_v, 4))
+        misaligned(lse, 4) || misaligned(descale_q, 4) || misaligned(descale_k, 4) || misaligned(descale_v, 4) ||
+        misaligned(cu_seqlens, 4))
         return FA_ERR_ALIGN;
-    const long long rows = static_cast<long long>(B) * N * H;
+    const bool packed = cu_seqlens != nullptr;
+    const long long rows = packed ? static_cast<long long>(N) * H : static_cast<long long>(B) * N * H;
     const long long elems = rows * d;
-    const long long vt_elems = static_cast<long long>(B) * H * d * fa_fp8_vt_stride(N);
-    if (elems <= 0 || elems > (1LL << 46) || !token_stride_ok(H, d) ||
-        static_cast<long long>(d) * fa_fp8_vt_stride(N) > 0x7fffffffLL)
+    const int vts = packed ? fa_fp8_vt_stride_packed(N, B) : fa_fp8_vt_stride(N);
+    const long long vt_elems = packed ? static_cast<long long>(H) * d * vts : static_cast<long long>(B) * H * d * vts;
+    // a head's V^T rows are addressed by one buffer resource (32-bit size)
+    if (elems <= 0 || elems > (1LL << 46) || !token_stride_ok(H, d) || vts == 0 ||
+        static_cast<long long>(d) * vts > 0x7fffffffLL || vt_elems > (1LL << 46))
         return FA_ERR_SHAPE;
     const size_t qb = static_cast<size_t>(elems), vb = static_cast<size_t>(vt_elems);
     const size_t ob = static_cast<size_t>(elems) * 2, lb = static_cast<size_t>(rows) * 4;
@@ -498,8 +539,12 @@ int fa_fwd_fp8(const void *q8, const void *k8, const void *vt8, const float *des
     for (int i = 0; i < 6; ++i)
         if (overlap(o, ob, ins[i], in_bytes[i]) || overlap(lse, lb, ins[i], in_bytes[i])) return FA_ERR_ALIAS;
     if (overlap(o, ob, lse, lb)) return FA_ERR_ALIAS;
+    if (packed) {
+        const size_t cb = static_cast<size_t>(B + 1) * 4;
+        if (overlap(o, ob, cu_seqlens, cb) || overlap(lse, lb, cu_seqlens, cb)) return FA_ERR_ALIAS;
+    }
 
-    Fp8Params fp;
+    Fp8Params fp{};
     fp.q = static_cast<const uint8_t *>(q8);
     fp.k = static_cast<const uint8_t *>(k8);
     fp.vt = static_cast<const uint8_t *>(vt8);
@@ -508,18 +553,39 @@ int fa_fwd_fp8(const void *q8, const void *k8, const void *vt8, const float *des
     fp.dv = descale_v;
     fp.o = static_cast<uint16_t *>(o);
     fp.lse = lse;
+    fp.cu = cu_seqlens;
     fp.B = B;
     fp.H = H;
     fp.N = N;
+    fp.vts = packed ? vts : 0;
     fp.cs = scale * kLog2e;
     const int rows_per_tile = fp8_rows_for(d);
     const long long n_qt = (static_cast<long long>(N) + rows_per_tile - 1) / rows_per_tile;
-    const long long grid = static_cast<long long>(B) * H * n_qt;
+    // packed: a bound on sum_b ceil(n_b / rows), surplus workgroups exit
+    const long long grid = packed ? static_cast<long long>(H) * (n_qt + B) : static_cast<long long>(B) * H * n_qt;
     if (grid <= 0 || grid > 0x7fffffffLL) return FA_ERR_SHAPE;
-    const KernelFp8Fn fn = d == 64 ? select_fp8_d64(causal != 0) : select_fp8_d128(causal != 0);
+    const KernelFp8Fn fn = d == 64    ? select_fp8_d64(causal != 0, packed)
+                           : d == 128 ? select_fp8_d128(causal != 0, packed)
+                                      : select_fp8_d256(causal != 0, packed);
     (void)hipGetLastError();
     hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(grid)), dim3(rows_per_tile * 2), 0, stream, fp);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_fp8(const void *q8, const void *k8, const void *vt8, const float *descale_q, const float *descale_k,
+               const float *descale_v, void *o, float *lse, int B, int H, int N, int d, float scale, int causal,
+               hipStream_t stream) {
+    return fwd_fp8_impl(q8, k8, vt8, descale_q, descale_k, descale_v, o, lse, nullptr, B, H, N, d, scale, causal,
+                        stream);
+}
+
+int fa_fwd_fp8_packed(const void *q8, const void *k8, const void *vt8, const float *descale_q,
+                      const float *descale_k, const float *descale_v, void *o, float *lse,
+                      const int32_t *cu_seqlens, int B, int H, int T, int d, float scale, int causal,
+                      hipStream_t stream) {
+    if (!cu_seqlens) return FA_ERR_NULLPTR;
+    return fwd_fp8_impl(q8, k8, vt8, descale_q, descale_k, descale_v, o, lse, cu_seqlens, B, H, T, d, scale,
+                        causal, stream);
 }
 
 int fa_fwd_variant(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,

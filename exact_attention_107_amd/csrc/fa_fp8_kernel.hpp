@@ -26,8 +26,14 @@
 //  * Software pipeline as in the bf16 kernel: the S(j+1) MFMAs are issued
 //    before the weights of S(j) are computed, the P V(j) MFMAs before the row
 //    max of S(j+1).
-// LDS rows are 64 or 128 bytes; their 16-byte chunks are XOR-permuted so
-// that the 16 rows of one fragment read cover 16 distinct bank groups.
+// LDS rows are 64, 128 or 256 bytes; their 16-byte chunks are XOR-permuted
+// so that the 16 rows of one fragment read cover 16 distinct bank groups.
+//
+// Packed sequences (cu_seqlens): each sequence is its own problem with its
+// own per-head scales; work items are decoded like the bf16 packed forward's.
+// V^T is [H, d, vts] with each sequence's keys starting at a multiple of 64
+// (the sum of the padded lengths of the sequences before it), so that a
+// 64-key tile again never crosses a sequence and its tail holds zero codes.
 
 #pragma once
 
@@ -40,11 +46,12 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 constexpr int kFp8Keys = 64;            // keys per K / V^T tile
 constexpr float kFp8PScale = 256.0f;    // P is stored as E4M3(2^8 P)
 
-// chunk permutation of row r for rows of RB bytes (RB = 64 or 128)
+// chunk permutation of row r for rows of RB bytes (RB = 64, 128 or 256)
 template <int RB>
 __device__ __forceinline__ int fp8_swz(int r) {
-    if constexpr (RB == 128) return (r >> 1) & 7;  // 2 rows per 256-byte bank window
-    else return (r >> 2) & 3;                      // 4 rows per window
+    if constexpr (RB == 256) return r & 15;             // one row per 256-byte bank window
+    else if constexpr (RB == 128) return (r >> 1) & 7;  // 2 rows per window
+    else return (r >> 2) & 3;                           // 4 rows per window
 }
 
 // 4 E4M3 codes of a, b, c, d (nearest even; |x| <= 448 required)
@@ -53,8 +60,23 @@ __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
     return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
 }
 
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(Fp8Geometry<D>::kWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+// Column of sequence b's first key in a packed V^T row: the sum of
+// ceil(n / 64) * 64 over the sequences before it (the host bounds the total
+// below 2^31), summed 64 sequences at a time by the wave.
+__device__ __forceinline__ int fp8_packed_vt_start(const int32_t *cu, int b) {
+    const int lane = threadIdx.x & 63;
+    int s = 0;
+    for (int o0 = 0; o0 < b; o0 += 64) {
+        const int o = o0 + lane;
+        int v = o < b ? (cu[o + 1] - cu[o] + 63) / 64 * 64 : 0;
+        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+        s += v;
+    }
+    return __builtin_amdgcn_readfirstlane(s);
+}
+
+template <int D, bool CAUSAL, bool PACKED>
+__global__ void __launch_bounds__(Fp8Geometry<D>::kWaves * 64) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
 fa_fp8_fwd_kernel(Fp8Params p) {
     constexpr int NW = Fp8Geometry<D>::kWaves, BC = kFp8Keys, BR = NW * 32;
     constexpr int KS = D / 64;          // 64-wide k steps of Q K^T
@@ -68,30 +90,43 @@ fa_fp8_fwd_kernel(Fp8Params p) {
 
     __shared__ __attribute__((aligned(1024))) char k_lds0[KT], k_lds1[KT], v_lds0[VT], v_lds1[VT];
 
-    const int BH = p.B * p.H;
-    const int n = p.N;
-    const int n_qt = (n + BR - 1) / BR;
-    int bh, qt;
-    if constexpr (CAUSAL) {
-        qt = n_qt - 1 - static_cast<int>(blockIdx.x) / BH;  // longest first
-        bh = blockIdx.x - (n_qt - 1 - qt) * BH;
-    } else {
-        const int G = gridDim.x, x = blockIdx.x & 7, sx = blockIdx.x >> 3;
-        const int per = G >> 3, rem = G & 7;
-        const int item = x * per + (x < rem ? x : rem) + sx;
-        bh = item / n_qt;
-        qt = item - bh * n_qt;
+    // work item (sequence b, head h, query tile qt), in the bf16 forward's
+    // order: dense causal longest first, dense non-causal in per-XCD runs,
+    // packed by sequence through cu_seqlens (surplus workgroups exit)
+    Work w;
+    {
+        Params wp{};
+        wp.B = p.B;
+        wp.H = p.H;
+        wp.N = p.N;
+        wp.cu = p.cu;
+        wp.n_qt = (p.N + BR - 1) / BR;
+        if (!decode_work<CAUSAL, PACKED, BR, false>(wp, w)) return;
     }
-    const int b = bh / p.H, h = bh - b * p.H;
+    const int b = w.b, h = w.h, qt = w.qt, n = w.n;
+    const int bh = b * p.H + h;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 31, hh = lane >> 5;
     const int q0 = qt * BR;
     const int wrow0 = q0 + wave * 32;
     const int rs = p.H * D;                                   // token stride of q8, k8 (bytes)
-    const long long base8 = (static_cast<long long>(b) * n * p.H + h) * D;
-    const int np = (n + 63) / 64 * 64;                        // V^T row stride (bytes)
-    const uint8_t *vt = p.vt + static_cast<long long>(bh) * D * np;  // V^T rows of (b, h)
+    const long long base8 = (w.t0 * p.H + h) * D;             // token 0 of the sequence, head h
+    // V^T: row stride np (bytes), the sequence's first key in the head's row
+    // 0 at vt, and the bytes from there to the end of the head's rows
+    int np;
+    const uint8_t *vt;
+    long long vspan;
+    if constexpr (PACKED) {
+        np = p.vts;
+        const int start = fp8_packed_vt_start(p.cu, b);
+        vt = p.vt + static_cast<long long>(h) * D * np + start;
+        vspan = static_cast<long long>(D) * np - start;
+    } else {
+        np = (n + 63) / 64 * 64;
+        vt = p.vt + static_cast<long long>(bh) * D * np;
+        vspan = static_cast<long long>(D) * np;
+    }
 
     // per-(b, h) scales: scores by scale * dq * dk (log2 units), output by dv
     const float cs = p.cs * p.dq[bh] * p.dk[bh];
@@ -249,7 +284,7 @@ fa_fp8_fwd_kernel(Fp8Params p) {
         // V^T rows are np bytes apart, so a 64-key tile never crosses a row;
         // keys past n hold the zero padding.  The scalar offset (d rows) stays
         // inside the head's D x np bytes, which the resource spans.
-        const auto vrs = make_rsrc(vt + kv0, (long long)D * np - kv0);
+        const auto vrs = make_rsrc(vt + kv0, vspan - kv0);
 #pragma unroll
         for (int i = 0; i < VBLK / NW; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, LDS_PTR(void, vd + (wave + NW * i) * 1024), 16, vvo,
@@ -295,7 +330,7 @@ fa_fp8_fwd_kernel(Fp8Params p) {
     // epilogue: O = O^T dv / l (l sums 2^8 P like O), LSE = (m + log2 l - 8) ln 2
     const float l = xhalf_sum(l_run);
     const float inv = l > 0.0f ? dv / l : 0.0f;
-    const long long obase = (static_cast<long long>(b) * n * p.H + h) * D;
+    const long long obase = (w.t0 * p.H + h) * D;
     const auto ors = make_rsrc(p.o + obase + static_cast<long long>(wrow0) * p.H * D,
                                (long long)(n - wrow0) * p.H * D * 2);
     const int voff_o = c * p.H * D * 2;
@@ -309,8 +344,10 @@ fa_fp8_fwd_kernel(Fp8Params p) {
             __builtin_amdgcn_raw_buffer_store_b64(v2, ors, voff_o + col * 2, 0, 0);
         }
     const int qrow = wrow0 + c;
+    // LSE row of the sequence's first token: dense [B, H, N], packed [H, T]
+    const long long lrow0 = PACKED ? static_cast<long long>(h) * p.N + w.t0 : static_cast<long long>(bh) * n;
     if (qrow < n && hh == 0)
-        p.lse[static_cast<long long>(bh) * n + qrow] = l > 0.0f ? (m_run + log2f(l) - 8.0f) * kLn2 : -INFINITY;
+        p.lse[lrow0 + qrow] = l > 0.0f ? (m_run + log2f(l) - 8.0f) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -392,9 +429,76 @@ __global__ void __launch_bounds__(256) fa_fp8_quant_kernel(QuantParams p) {
     }
 }
 
+// Packed sequences: one workgroup per (sequence, head).  amax over the
+// sequence's tokens, then its codes: [T, H, d] in place of x, or the
+// sequence's columns of the packed V^T rows (zero codes up to the next
+// multiple of 64 keys; columns past the last sequence's padding are not
+// written).
+__global__ void __launch_bounds__(256) fa_fp8_amax_packed_kernel(QuantParams p) {
+    const int bh = blockIdx.x;
+    const int b = bh / p.H, h = bh - b * p.H;
+    const int t0 = p.cu[b], n = p.cu[b + 1] - t0;
+    const int chunks = p.d / 8;
+    const long long total = static_cast<long long>(n) * chunks;
+    float m = 0.0f;
+    for (long long t = threadIdx.x; t < total; t += 256) {
+        const long long i = t / chunks;
+        const int cc = static_cast<int>(t - i * chunks);
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(p.x + ((t0 + i) * p.H + h) * p.d + cc * 8);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            m = fmaxf(m, fabsf(__uint_as_float(w[k] << 16)));
+            m = fmaxf(m, fabsf(__uint_as_float(w[k] & 0xffff0000u)));
+        }
+    }
+    __shared__ float red[256];
+    red[threadIdx.x] = m;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if (threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) p.descale[bh] = red[0] > 0.0f ? red[0] / 448.0f : 1.0f;
+}
+
+__global__ void __launch_bounds__(256) fa_fp8_quant_packed_kernel(QuantParams p) {
+    const int bh = blockIdx.x;
+    const int b = bh / p.H, h = bh - b * p.H;
+    const int t0 = p.cu[b], n = p.cu[b + 1] - t0;
+    const int q4 = p.d / 4;
+    const float inv = 1.0f / p.descale[bh];
+    auto codes_of = [&](long long tok, int cq) {
+        const u32x2 w = *reinterpret_cast<const u32x2 *>(p.x + (tok * p.H + h) * p.d + cq * 4);
+        return pack_fp8x4(__uint_as_float(w[0] << 16) * inv, __uint_as_float(w[0] & 0xffff0000u) * inv,
+                          __uint_as_float(w[1] << 16) * inv, __uint_as_float(w[1] & 0xffff0000u) * inv);
+    };
+    if (!p.transpose) {
+        const long long total = static_cast<long long>(n) * q4;
+        for (long long t = threadIdx.x; t < total; t += 256) {
+            const long long i = t / q4;
+            const int cq = static_cast<int>(t - i * q4);
+            *reinterpret_cast<int *>(p.x8 + ((t0 + i) * p.H + h) * p.d + cq * 4) = codes_of(t0 + i, cq);
+        }
+        return;
+    }
+    // transposed: lanes run along the sequence's (padded) keys
+    const int pad = (n + 63) / 64 * 64;
+    const int start = fp8_packed_vt_start(p.cu, b);
+    const long long total = static_cast<long long>(pad) * q4;
+    for (long long t = threadIdx.x; t < total; t += 256) {
+        const int cq = static_cast<int>(t / pad);
+        const int u = static_cast<int>(t - static_cast<long long>(cq) * pad);
+        const int codes = u < n ? codes_of(t0 + u, cq) : 0;
+        uint8_t *row = p.x8 + (static_cast<long long>(h) * p.d + cq * 4) * p.vts + start + u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) row[static_cast<long long>(k) * p.vts] = static_cast<uint8_t>(codes >> (8 * k));
+    }
+}
+
 template <int D>
-KernelFp8Fn select_fp8(bool causal) {
-    return causal ? fa_fp8_fwd_kernel<D, true> : fa_fp8_fwd_kernel<D, false>;
+KernelFp8Fn select_fp8(bool causal, bool packed) {
+    if (packed) return causal ? fa_fp8_fwd_kernel<D, true, true> : fa_fp8_fwd_kernel<D, false, true>;
+    return causal ? fa_fp8_fwd_kernel<D, true, false> : fa_fp8_fwd_kernel<D, false, false>;
 }
 
 }  // namespace fa_detail

@@ -125,13 +125,16 @@ BwdKernels select_bwd_d256(bool causal, bool packed);
 
 // FP8 (E4M3) forward and quantisation (fa_fp8_kernel.hpp).
 struct Fp8Params {
-    const uint8_t *q, *k;   // E4M3 codes [B, N, H, d]
+    const uint8_t *q, *k;   // E4M3 codes [B, N, H, d] (packed: [T, H, d])
     const uint8_t *vt;      // E4M3 codes of V transposed, [B, H, d, Np],
-                            // Np = ceil(N / 64) * 64, zero padded
+                            // Np = ceil(N / 64) * 64, zero padded (packed:
+                            // [H, d, vts], each sequence padded to 64 keys)
     const float *dq, *dk, *dv;  // per-(b, h) descales [B * H]
-    uint16_t *o;            // bf16 [B, N, H, d]
-    float *lse;             // [B, H, N]
-    int B, H, N;
+    uint16_t *o;            // bf16 [B, N, H, d] (packed: [T, H, d])
+    float *lse;             // [B, H, N] (packed: [H, T])
+    const int32_t *cu;      // packed offsets [B + 1], or nullptr (dense)
+    int B, H, N;            // N: sequence length (dense) or total tokens T (packed)
+    int vts;                // packed: V^T row length in keys
     float cs;               // scale * log2(e)
 };
 using KernelFp8Fn = void (*)(Fp8Params);
@@ -142,14 +145,19 @@ template <int D> struct Fp8Geometry {
     static constexpr int kWaves = 4;
     static constexpr int kRows = kWaves * 32;
 };
-inline int fp8_rows_for(int d) { return d == 128 ? Fp8Geometry<128>::kRows : Fp8Geometry<64>::kRows; }
-KernelFp8Fn select_fp8_d64(bool causal);
-KernelFp8Fn select_fp8_d128(bool causal);
+inline int fp8_rows_for(int d) {
+    return d == 64 ? Fp8Geometry<64>::kRows : d == 128 ? Fp8Geometry<128>::kRows : Fp8Geometry<256>::kRows;
+}
+KernelFp8Fn select_fp8_d64(bool causal, bool packed);
+KernelFp8Fn select_fp8_d128(bool causal, bool packed);
+KernelFp8Fn select_fp8_d256(bool causal, bool packed);
 struct QuantParams {
-    const uint16_t *x;      // bf16 [B, N, H, d]
-    uint8_t *x8;            // E4M3 codes [B, N, H, d] or [B, H, d, Np]
+    const uint16_t *x;      // bf16 [B, N, H, d] (packed: [T, H, d])
+    uint8_t *x8;            // E4M3 codes [B, N, H, d] or [B, H, d, Np] (packed: [T, H, d] or [H, d, vts])
     float *descale;         // [B * H]
+    const int32_t *cu;      // packed offsets [B + 1], or nullptr (dense)
     int B, H, N, d, transpose;
+    int vts;                // packed V^T row length in keys
 };
 int launch_quant(const QuantParams &qp, void *stream);
 

@@ -672,7 +672,7 @@ fa_fwd_kernel(Params p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int C = kb2 * 32 + (r >> 2) * 8 + (r & 3);
-                    s[b][kb2][r] = (C >= lo) & (C < hi) ? s[b][kb2][r] : -INFINITY;
+                    s[b][kb2][r] = ((C >= lo) & (C < hi)) ? s[b][kb2][r] : -INFINITY;
                 }
         }
     };

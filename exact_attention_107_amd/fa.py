@@ -22,7 +22,8 @@ RESCALE_ALWAYS, RESCALE_STRICT, RESCALE_THRESHOLD = 0, 1, 2
 EXPORTS = ("fa_fwd", "fa_fwd_variant", "fa_strerror", "fa_tile_rows", "fa_tile_keys",
            "fa_fwd_splitkv", "fa_merge", "fa_split_range", "fa_num_splits", "fa_bwd",
            "fa_bwd_workspace_floats", "fa_fwd_fp8", "fa_quantize_fp8", "fa_fp8_vt_stride",
-           "fa_fwd_masked", "fa_fwd_rescale_counts", "fa_fwd_splitkv_static", "fa_fwd_pingpong")
+           "fa_fwd_masked", "fa_fwd_rescale_counts", "fa_fwd_splitkv_static", "fa_fwd_pingpong",
+           "fa_fp8_vt_stride_packed", "fa_quantize_fp8_packed", "fa_fwd_fp8_packed")
 FA_ERR_SCRATCH = 10
 STATIC_SCRATCH_BYTES = 64 << 20   # FA_STATIC_SCRATCH_BYTES of include/fa.h
 
@@ -78,6 +79,12 @@ def load(path: str | None = None):
     lib.fa_quantize_fp8.restype = i32
     lib.fa_fp8_vt_stride.argtypes = [i32]
     lib.fa_fp8_vt_stride.restype = i32
+    lib.fa_fp8_vt_stride_packed.argtypes = [i32, i32]
+    lib.fa_fp8_vt_stride_packed.restype = i32
+    lib.fa_quantize_fp8_packed.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    lib.fa_quantize_fp8_packed.restype = i32
+    lib.fa_fwd_fp8_packed.argtypes = [vp] * 9 + [i32, i32, i32, i32, ctypes.c_float, i32, vp]
+    lib.fa_fwd_fp8_packed.restype = i32
     lib.fa_fwd_masked.argtypes = [vp] * 5 + [i32, i32, i32, i32, ctypes.c_float, i32, i32, vp, vp]
     lib.fa_fwd_masked.restype = i32
     lib.fa_fwd_pingpong.argtypes = common
@@ -481,6 +488,88 @@ def fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, vt8: torch.Tensor, descale_q: to
                             descale_k.data_ptr(), descale_v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                             B, H, N, d, ctypes.c_float(scale), int(bool(causal)),
                             ctypes.c_void_p(s.cuda_stream))
+    if rc != 0:
+        raise FaError(rc, strerror(rc))
+    return out, lse
+
+
+def fp8_vt_stride_packed(T: int, B: int) -> int:
+    return int(load().fa_fp8_vt_stride_packed(int(T), int(B)))
+
+
+def _packed_cu(cu_seqlens, dev):
+    _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be int32 [B+1]")
+    return cu_seqlens.numel() - 1
+
+
+def quantize_fp8_packed(x: torch.Tensor, cu_seqlens: torch.Tensor, *, transpose: bool = False,
+                        out: torch.Tensor | None = None, descale: torch.Tensor | None = None,
+                        stream: torch.cuda.Stream | None = None):
+    """Per-(sequence, head) E4M3 quantisation of packed bf16 ``x [T, H, d]``
+    (``fa_quantize_fp8_packed``).  Returns uint8 codes ``[T, H, d]`` (or the
+    packed V^T layout ``[H, d, fp8_vt_stride_packed(T, B)]`` when
+    ``transpose``) and fp32 ``descale [B, H]``."""
+    lib = load()
+    dev = x.device
+    _check(x, "x", torch.bfloat16, dev)
+    if x.dim() != 3:
+        raise ValueError("packed x must be [T, H, d]")
+    T, H, d = (int(v) for v in x.shape)
+    B = _packed_cu(cu_seqlens, dev)
+    shape = (H, d, fp8_vt_stride_packed(T, B)) if transpose else (T, H, d)
+    # the columns past the last sequence's padding are not written: zero them
+    out = (torch.zeros if transpose else torch.empty)(shape, dtype=torch.uint8, device=dev) if out is None else out
+    descale = torch.empty((B, H), dtype=torch.float32, device=dev) if descale is None else descale
+    _check(out, "out", torch.uint8, dev)
+    _check(descale, "descale", torch.float32, dev)
+    if tuple(out.shape) != shape or tuple(descale.shape) != (B, H):
+        raise ValueError(f"out must be {shape} and descale {(B, H)}")
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = lib.fa_quantize_fp8_packed(x.data_ptr(), out.data_ptr(), descale.data_ptr(), cu_seqlens.data_ptr(),
+                                        B, H, T, d, int(bool(transpose)), ctypes.c_void_p(s.cuda_stream))
+    if rc != 0:
+        raise FaError(rc, strerror(rc))
+    return out, descale
+
+
+def fwd_fp8_packed(q8: torch.Tensor, k8: torch.Tensor, vt8: torch.Tensor, descale_q: torch.Tensor,
+                   descale_k: torch.Tensor, descale_v: torch.Tensor, cu_seqlens: torch.Tensor, *,
+                   causal: bool = False, scale: float | None = None, out: torch.Tensor | None = None,
+                   lse: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None):
+    """FP8 forward over packed sequences (``fa_fwd_fp8_packed``): E4M3 ``q8,
+    k8 [T, H, d]``, ``vt8 [H, d, fp8_vt_stride_packed(T, B)]``, fp32 descales
+    ``[B, H]``.  Returns bf16 ``o [T, H, d]`` and fp32 ``lse [H, T]``."""
+    lib = load()
+    dev = q8.device
+    for t, name in ((q8, "q8"), (k8, "k8"), (vt8, "vt8")):
+        _check(t, name, torch.uint8, dev)
+    if q8.dim() != 3:
+        raise ValueError("packed q8 must be [T, H, d]")
+    T, H, d = (int(v) for v in q8.shape)
+    B = _packed_cu(cu_seqlens, dev)
+    if tuple(k8.shape) != (T, H, d) or tuple(vt8.shape) != (H, d, fp8_vt_stride_packed(T, B)):
+        raise ValueError("k8 must be like q8 and vt8 [H, d, fp8_vt_stride_packed(T, B)]")
+    for t, name in ((descale_q, "descale_q"), (descale_k, "descale_k"), (descale_v, "descale_v")):
+        _check(t, name, torch.float32, dev)
+        if tuple(t.shape) != (B, H):
+            raise ValueError(f"{name} must be {(B, H)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev) if out is None else out
+    lse = torch.empty((H, T), dtype=torch.float32, device=dev) if lse is None else lse
+    _check(out, "out", torch.bfloat16, dev)
+    _check(lse, "lse", torch.float32, dev)
+    if tuple(out.shape) != (T, H, d) or tuple(lse.shape) != (H, T):
+        raise ValueError(f"out must be {(T, H, d)} and lse {(H, T)}")
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = lib.fa_fwd_fp8_packed(q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), descale_q.data_ptr(),
+                                   descale_k.data_ptr(), descale_v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                   cu_seqlens.data_ptr(), B, H, T, d, ctypes.c_float(scale), int(bool(causal)),
+                                   ctypes.c_void_p(s.cuda_stream))
     if rc != 0:
         raise FaError(rc, strerror(rc))
     return out, lse

@@ -329,7 +329,7 @@ int fa_fwd_masked(const void *q, const void *k, const void *v, void *o,
                   hipStream_t stream);
 
 /*
- * FP8 forward (dense layout, d = 64 or 128).  The FlashAttention-3 notes of
+ * FP8 forward (dense layout, d = 64, 128 or 256).  The FlashAttention-3 notes of
  * "FlashAttention 1-4 explained" run the forward's products on FP8 matrix
  * units; here Q K^T and P V both run on E4M3 operands (OCP E4M3: bias 7,
  * largest finite 448, 0x7f/0xff NaN) with fp32 accumulation.  Scaling is per
@@ -364,6 +364,56 @@ int fa_quantize_fp8(const void *x, void *x8, float *descale, int B, int H,
 
 /* Row stride (keys) of the transposed FP8 V layout: ceil(N / 64) * 64. */
 int fa_fp8_vt_stride(int N);
+
+/*
+ * Packed sequences in FP8 ("Understanding FlashAttention V4", section 3.4,
+ * names variable-length sequences as a case of the tile scheduler): B
+ * sequences in T tokens, cu_seqlens as fa_fwd's (device int32 [B + 1],
+ * cu_seqlens[0] = 0, non-decreasing, cu_seqlens[B] = T; read on the device,
+ * not validated).  Each sequence is its own attention problem with its own
+ * per-head scales.
+ *
+ * fa_fp8_vt_stride_packed: row length (keys) of the packed transposed V
+ * layout [H, d, Tp]: Tp = ceil(T / 64) * 64 + 64 B, which holds every
+ * sequence's keys padded to a multiple of 64; 0 for T < 1, B < 1 or a
+ * length past 2^31 - 1.  Sequence b's keys start at column
+ * sum_{b' < b} ceil(n_b' / 64) * 64.
+ */
+int fa_fp8_vt_stride_packed(int T, int B);
+
+/*
+ * fa_quantize_fp8_packed: fa_quantize_fp8 per (sequence, head) of a packed
+ * bf16 x [T, H, d]: descale[b * H + h] = amax / 448 over sequence b's tokens
+ * of head h (1 when all zero or the sequence is empty).  transpose = 0
+ * writes x8 as [T, H, d]; transpose != 0 writes the packed V^T layout
+ * [H, d, fa_fp8_vt_stride_packed(T, B)]: sequence b's codes and zero codes up
+ * to its next multiple of 64 keys; the columns past the last sequence's
+ * padding are not written.  One workgroup per (sequence, head) for each of
+ * the two kernels on `stream`.  Errors as fa_quantize_fp8; FA_ERR_NULLPTR
+ * for cu_seqlens == NULL.
+ */
+int fa_quantize_fp8_packed(const void *x, void *x8, float *descale,
+                           const int32_t *cu_seqlens, int B, int H, int T,
+                           int d, int transpose, hipStream_t stream);
+
+/*
+ * fa_fwd_fp8_packed: fa_fwd_fp8 over packed sequences.
+ *   q8, k8     device E4M3 codes [T, H, d].
+ *   vt8        device E4M3 codes in the packed V^T layout
+ *              [H, d, fa_fp8_vt_stride_packed(T, B)]; each sequence's padding
+ *              columns must hold finite codes (fa_quantize_fp8_packed writes 0).
+ *   descale_q, descale_k, descale_v   device fp32 [B * H] per (sequence, head).
+ *   o, lse     device outputs: bf16 [T, H, d], fp32 [H, T].
+ *   cu_seqlens, B, T   as above; H, d, scale, causal, stream as fa_fwd_fp8.
+ * Work items are (sequence, head, query tile) decoded from cu_seqlens like
+ * the packed fa_fwd.  Errors as fa_fwd_fp8; FA_ERR_NULLPTR for
+ * cu_seqlens == NULL.
+ */
+int fa_fwd_fp8_packed(const void *q8, const void *k8, const void *vt8,
+                      const float *descale_q, const float *descale_k,
+                      const float *descale_v, void *o, float *lse,
+                      const int32_t *cu_seqlens, int B, int H, int T, int d,
+                      float scale, int causal, hipStream_t stream);
 
 /* Static, NUL-terminated description of an fa_status code. */
 const char *fa_strerror(int code);

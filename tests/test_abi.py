@@ -337,3 +337,69 @@ def call_ping(lib, q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, N=64, d=128, scale=0.125
 ])
 def test_pingpong_invalid_arguments_are_rejected(lib, kw, code):
     assert call_ping(lib, **kw) == code
+
+
+# ---------------------------------------------------------------------------
+# FP8 over packed sequences
+
+DSQ, DSK, DSV, CU8 = 0x600000, 0x610000, 0x620000, 0x700000
+
+
+def test_fp8_vt_stride_packed(lib):
+    assert fa.fp8_vt_stride_packed(1, 1) == 128
+    assert fa.fp8_vt_stride_packed(100, 3) == 128 + 192
+    assert fa.fp8_vt_stride_packed(64, 1) == 128
+    assert fa.fp8_vt_stride_packed(0, 1) == 0 and fa.fp8_vt_stride_packed(5, 0) == 0
+    assert fa.fp8_vt_stride_packed((1 << 31) - 64, 2) == 0      # past 2^31 - 1
+
+
+def call_q8p(lib, x=Q, x8=K, ds=DSQ, cu=CU8, B=2, H=2, T=100, d=128, transpose=0):
+    return lib.fa_quantize_fp8_packed(*(ctypes.c_void_p(a) if a else None for a in (x, x8, ds, cu)), B, H, T, d,
+                                      transpose, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=0), NULLPTR), (dict(x=0), NULLPTR), (dict(ds=0), NULLPTR), (dict(T=0), SHAPE), (dict(B=0), SHAPE),
+    (dict(d=96), HEAD_DIM), (dict(cu=CU8 + 2), ALIGN), (dict(x=Q + 8), ALIGN), (dict(x8=Q + 1024), ALIAS),
+    (dict(ds=CU8), ALIAS), (dict(x8=CU8 - 64), ALIAS), (dict(transpose=1, T=(1 << 31) - 64), SHAPE),
+])
+def test_quantize_fp8_packed_invalid_arguments_are_rejected(lib, kw, code):
+    assert call_q8p(lib, **kw) == code
+
+
+def call_f8p(lib, q8=Q, k8=K, vt8=V, dq=DSQ, dk=DSK, dv=DSV, o=O, lse=L, cu=CU8, B=2, H=2, T=100, d=128,
+             scale=0.125, causal=0):
+    return lib.fa_fwd_fp8_packed(*(ctypes.c_void_p(a) if a else None for a in (q8, k8, vt8, dq, dk, dv, o, lse, cu)),
+                                 B, H, T, d, ctypes.c_float(scale), causal, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=0), NULLPTR), (dict(vt8=0), NULLPTR), (dict(T=0), SHAPE), (dict(d=32), HEAD_DIM),
+    (dict(scale=-1.0), SCALE), (dict(cu=CU8 + 1), ALIGN), (dict(vt8=V + 4), ALIGN), (dict(o=V + 1024), ALIAS),
+    (dict(lse=DSK), ALIAS), (dict(o=CU8 - 64), ALIAS), (dict(lse=CU8), ALIAS),
+    # a head's V^T rows are one 32-bit buffer range: d * Tp < 2^31
+    (dict(d=256, T=1 << 23, H=1, q8=1 << 40, k8=2 << 40, vt8=3 << 40, o=4 << 40, lse=5 << 40), SHAPE),
+])
+def test_fwd_fp8_packed_invalid_arguments_are_rejected(lib, kw, code):
+    assert call_f8p(lib, **kw) == code
+
+
+def test_fp8_packed_binding_checks_shapes():
+    """Wrong packed shapes are refused before the library is called (host
+    tensors: nothing may reach a kernel)."""
+    import torch
+    T, H, d = 100, 2, 64
+    cu = torch.tensor([0, 40, 100], dtype=torch.int32)
+    q8 = torch.zeros(T, H, d, dtype=torch.uint8)
+    vt_bad = torch.zeros(H, d, fa.fp8_vt_stride(T), dtype=torch.uint8)   # the dense stride
+    ds = torch.ones(2, H, dtype=torch.float32)
+    with pytest.raises(ValueError, match="vt8"):
+        fa.fwd_fp8_packed(q8, q8, vt_bad, ds, ds, ds, cu)
+    vt8 = torch.zeros(H, d, fa.fp8_vt_stride_packed(T, 2), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="descale_q"):
+        fa.fwd_fp8_packed(q8, q8, vt8, torch.ones(1, H), ds, ds, cu)
+    with pytest.raises(ValueError, match="out must be"):
+        fa.fwd_fp8_packed(q8, q8, vt8, ds, ds, ds, cu, out=torch.empty(T - 1, H, d, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="out must be"):
+        fa.quantize_fp8_packed(torch.zeros(T, H, d, dtype=torch.bfloat16), cu,
+                               out=torch.empty(T, H, d - 1, dtype=torch.uint8))
