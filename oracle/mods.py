@@ -76,3 +76,53 @@ def attention(q, k, v, *, scale: float, left: int = -1, right: int = -1, slopes=
     for r, (b, h, i) in enumerate(rows):
         o[r], lse[r] = one(b, h, i)
     return o, lse
+
+
+def attention_packed(q, k, v, cu_seqlens, *, scale: float, left: int = -1, right: int = -1, slopes=None,
+                     rows=None):
+    """The same definition over packed sequences: ``q, k, v [T, H, d]`` with
+    sequence b holding tokens ``cu[b] .. cu[b+1]-1``; positions i, j (window
+    and bias) count from the sequence's first token, and a query sees only its
+    own sequence's keys.
+
+    Returns ``(o [T, H, d], lse [H, T])``, or for ``rows`` (``(n, 3)``
+    triples (b, h, i), i within sequence b) ``(o [n, d], lse [n])``.
+    """
+    Q, K, V = (_widen(x) for x in (q, k, v))
+    T, H, d = Q.shape
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    n_seq = np.diff(cu)
+    if cu[0] != 0 or np.any(n_seq < 0) or cu[-1] != T:
+        raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at T")
+    sc = float(np.float32(scale))
+    sl = np.zeros(H) if slopes is None else np.asarray(slopes, np.float32).astype(np.float64)
+
+    def one(b, h, i):
+        t0, n = int(cu[b]), int(n_seq[b])
+        keys = np.arange(n)
+        s = (K[t0:t0 + n, h] @ Q[t0 + i, h]) * sc + sl[h] * (keys - i)
+        vis = visible(i, keys, n, left, right)
+        if not vis.any():
+            return np.zeros(d), -np.inf
+        s = np.where(vis, s, -np.inf)
+        m = s.max()
+        e = np.exp(s - m)
+        l = e.sum()
+        return (e / l) @ V[t0:t0 + n, h], m + np.log(l)
+
+    if rows is None:
+        o = np.zeros((T, H, d))
+        lse = np.zeros((H, T))
+        for b in range(len(n_seq)):
+            for h in range(H):
+                for i in range(int(n_seq[b])):
+                    o[cu[b] + i, h], lse[h, cu[b] + i] = one(b, h, i)
+        return o, lse
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1, 3)
+    o = np.zeros((len(rows), d))
+    lse = np.zeros(len(rows))
+    for r, (b, h, i) in enumerate(rows):
+        if not 0 <= i < n_seq[b]:
+            raise ValueError("row index outside its sequence")
+        o[r], lse[r] = one(b, h, i)
+    return o, lse

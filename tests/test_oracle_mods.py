@@ -99,7 +99,7 @@ MUTANTS = {
 def test_mods_mutant_is_caught(name, oracle_lib):
     old, new = MUTANTS[name]
     src = open(SRC).read()
-    assert src.count(old) == 1
+    assert src.count(old) >= 1      # the dense and the packed form share the score line
     mod = types.ModuleType(f"mods_{name}")
     mod.__dict__["_widen"] = oracle._widen
     exec(compile(src.replace(old, new).replace("from . import _widen", ""), name, "exec"), mod.__dict__)
@@ -111,3 +111,64 @@ def test_mods_mutant_is_caught(name, oracle_lib):
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, f"mutant {name} passed every pin"
+
+
+# ---------------------------------------------------------------------------
+# Packed sequences: each sequence is the dense problem of its own tokens.
+
+PACKED_LENGTHS = [7, 0, 1, 23, 16, 9]
+PACKED_CASES = [(-1, -1, None), (-1, 0, None), (3, 0, [0.5, 0.125]), (0, 2, None), (4, 5, [0.25, 0.0625]),
+                (6, -1, [0.125, 0.5])]
+
+
+def pin_packed_equals_dense_per_sequence(attn_packed):
+    inp = make_inputs(Run("mp", len(PACKED_LENGTHS), 2, 0, 16, False, 43, varlen=True), lengths=PACKED_LENGTHS)
+    cu = inp["cu_seqlens"]
+    for left, right, slopes in PACKED_CASES:
+        sl = None if slopes is None else np.array(slopes, np.float32)
+        o, l = attn_packed(inp["q"], inp["k"], inp["v"], cu, scale=0.3, left=left, right=right, slopes=sl)
+        rows = []
+        for b, n in enumerate(PACKED_LENGTHS):
+            if n == 0:
+                continue
+            t0 = int(cu[b])
+            one = {x: inp[x][None, t0:t0 + n] for x in ("q", "k", "v")}
+            ro, rl = omods.attention(one["q"], one["k"], one["v"], scale=0.3, left=left, right=right, slopes=sl)
+            assert np.max(np.abs(o[t0:t0 + n] - ro[0])) <= 1e-12, (left, right, b)
+            ok = np.isfinite(rl[0])
+            assert np.array_equal(ok, np.isfinite(l[:, t0:t0 + n]))
+            assert np.max(np.abs(l[:, t0:t0 + n][ok] - rl[0][ok]), initial=0) <= 1e-12, (left, right, b)
+            rows += [[b, 1, n - 1], [b, 0, n // 2]]
+        rows = np.array(rows)
+        orow, lrow = attn_packed(inp["q"], inp["k"], inp["v"], cu, scale=0.3, left=left, right=right, slopes=sl,
+                                 rows=rows)
+        tok = cu[rows[:, 0]] + rows[:, 2]
+        assert np.array_equal(orow, o[tok, rows[:, 1]]) and np.array_equal(lrow, l[rows[:, 1], tok])
+
+
+def test_packed_mods_pin():
+    pin_packed_equals_dense_per_sequence(omods.attention_packed)
+
+
+PACKED_MUTANTS = {
+    # positions counted from the batch's first token instead of the sequence's
+    "global_bias_position": ("+ sl[h] * (keys - i)\n        vis = visible(i, keys, n, left, right)",
+                             "+ sl[h] * (keys - i - t0)\n        vis = visible(i, keys, n, left, right)"),
+    "global_window_position": ("vis = visible(i, keys, n, left, right)", "vis = visible(i + t0, keys, n, left, right)"),
+    # one token too many: the next sequence's first token is visible
+    "key_past_sequence": ("t0, n = int(cu[b]), int(n_seq[b])",
+                          "t0, n = int(cu[b]), min(int(n_seq[b]) + 1, T - int(cu[b]))"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PACKED_MUTANTS))
+def test_packed_mods_mutant_is_caught(name):
+    old, new = PACKED_MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, name
+    mod = types.ModuleType(f"mods_{name}")
+    mod.__dict__["_widen"] = oracle._widen
+    exec(compile(src.replace(old, new).replace("from . import _widen", ""), name, "exec"), mod.__dict__)
+    with pytest.raises((AssertionError, IndexError, ValueError)):
+        with np.errstate(all="ignore"):
+            pin_packed_equals_dense_per_sequence(mod.attention_packed)
