@@ -221,16 +221,18 @@ int fa_merge(const float *o_part, const float *lse_part, int num_splits, int B, 
 
 // Validation shared by the two split-KV entry points (everything but the
 // workspaces).
-static int splitkv_check(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
-                         int d, float scale, int num_splits) {
+// (Packed: cu_seqlens != nullptr and N = T tokens; rows = T H.)
+static int splitkv_check(const void *q, const void *k, const void *v, void *o, float *lse, const int32_t *cu,
+                         int B, int H, int N, int d, float scale, int num_splits) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULLPTR;
     if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
     if (d != 64 && d != 128 && d != 256) return FA_ERR_HEAD_DIM;
     if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_SCALE;
     if (num_splits < 1 || num_splits > key_tiles(N)) return FA_ERR_SPLIT;
-    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) || misaligned(lse, 4))
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) || misaligned(lse, 4) ||
+        misaligned(cu, 4))
         return FA_ERR_ALIGN;
-    const long long rows = static_cast<long long>(B) * N * H;
+    const long long rows = cu ? static_cast<long long>(N) * H : static_cast<long long>(B) * N * H;
     const long long elems = rows * d;
     if (elems <= 0 || elems * num_splits > (1LL << 46) || !token_stride_ok(H, d)) return FA_ERR_SHAPE;
     const size_t tb = static_cast<size_t>(elems) * 2, lb = static_cast<size_t>(rows) * 4;
@@ -238,14 +240,19 @@ static int splitkv_check(const void *q, const void *k, const void *v, void *o, f
     for (const void *in : ins)
         if (overlap(o, tb, in, tb) || overlap(lse, lb, in, tb)) return FA_ERR_ALIAS;
     if (overlap(o, tb, lse, lb)) return FA_ERR_ALIAS;
+    if (cu) {
+        const size_t cb = static_cast<size_t>(B + 1) * 4;
+        if (overlap(o, tb, cu, cb) || overlap(lse, lb, cu, cb)) return FA_ERR_ALIAS;
+    }
     return FA_OK;
 }
 
 // The split forward and the merge on validated arguments.
-static int splitkv_launch(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
-                          int d, float scale, int causal, int num_splits, float *o_part, float *lse_part,
-                          hipStream_t stream) {
-    const long long rows = static_cast<long long>(B) * N * H;
+static int splitkv_launch(const void *q, const void *k, const void *v, void *o, float *lse, const int32_t *cu,
+                          int B, int H, int N, int d, float scale, int causal, int num_splits, float *o_part,
+                          float *lse_part, hipStream_t stream) {
+    const bool packed = cu != nullptr;
+    const long long rows = packed ? static_cast<long long>(N) * H : static_cast<long long>(B) * N * H;
     const long long elems = rows * d;
     Params prm{};
     prm.q = static_cast<const uint16_t *>(q);
@@ -253,7 +260,7 @@ static int splitkv_launch(const void *q, const void *k, const void *v, void *o, 
     prm.v = static_cast<const uint16_t *>(v);
     prm.o = static_cast<uint16_t *>(o);
     prm.lse = lse;
-    prm.cu = nullptr;
+    prm.cu = cu;
     prm.B = B;
     prm.H = H;
     prm.N = N;
@@ -264,19 +271,23 @@ static int splitkv_launch(const void *q, const void *k, const void *v, void *o, 
     prm.op = o_part;
     prm.lp = lse_part;
     prm.nsplit = num_splits;
-    const long long grid = static_cast<long long>(B) * H * n_qt * num_splits;
+    // packed: a bound on sum_b ceil(n_b / rows) query tiles, surplus workgroups exit
+    const long long items = packed ? static_cast<long long>(H) * (n_qt + B) : static_cast<long long>(B) * H * n_qt;
+    const long long grid = items * num_splits;
     if (grid <= 0 || grid > 0x7fffffffLL) return FA_ERR_SHAPE;
 
     KernelFn fn;
     switch (d) {
-        case 64: fn = select_split_d64(causal != 0); break;
-        case 128: fn = select_split_d128(causal != 0); break;
-        default: fn = select_split_d256(causal != 0); break;
+        case 64: fn = select_split_d64(causal != 0, packed); break;
+        case 128: fn = select_split_d128(causal != 0, packed); break;
+        default: fn = select_split_d256(causal != 0, packed); break;
     }
     (void)hipGetLastError();
     hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(grid)), dim3(waves_for(d) * 64), 0, stream, prm);
     if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
 
+    // the merge is per row: packed [T, H, d] / [H, T] is the dense layout
+    // of one sequence of T tokens
     MergeParams mp;
     mp.op = o_part;
     mp.lp = lse_part;
@@ -291,14 +302,15 @@ static int splitkv_launch(const void *q, const void *k, const void *v, void *o, 
     return launch_merge(mp, d, stream) == 0 ? FA_OK : FA_ERR_HIP;
 }
 
-int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
-                   int N, int d, float scale, int causal, int num_splits, float *o_part,
-                   float *lse_part, hipStream_t stream) {
+// Caller workspaces: validation and launch (dense or packed).
+static int splitkv_ws(const void *q, const void *k, const void *v, void *o, float *lse, const int32_t *cu, int B,
+                      int H, int N, int d, float scale, int causal, int num_splits, float *o_part, float *lse_part,
+                      hipStream_t stream) {
     if (!o_part || !lse_part) return FA_ERR_NULLPTR;
-    const int rc = splitkv_check(q, k, v, o, lse, B, H, N, d, scale, num_splits);
+    const int rc = splitkv_check(q, k, v, o, lse, cu, B, H, N, d, scale, num_splits);
     if (rc != FA_OK) return rc;
     if (misaligned(o_part, 16) || misaligned(lse_part, 4)) return FA_ERR_ALIGN;
-    const long long rows = static_cast<long long>(B) * N * H;
+    const long long rows = cu ? static_cast<long long>(N) * H : static_cast<long long>(B) * N * H;
     const long long elems = rows * d;
     const size_t tb = static_cast<size_t>(elems) * 2, lb = static_cast<size_t>(rows) * 4;
     const size_t opb = static_cast<size_t>(elems) * num_splits * 4, lpb = static_cast<size_t>(rows) * num_splits * 4;
@@ -308,12 +320,30 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
     if (overlap(o_part, opb, o, tb) || overlap(o_part, opb, lse, lb) || overlap(lse_part, lpb, o, tb) ||
         overlap(lse_part, lpb, lse, lb) || overlap(o_part, opb, lse_part, lpb))
         return FA_ERR_ALIAS;
-    return splitkv_launch(q, k, v, o, lse, B, H, N, d, scale, causal, num_splits, o_part, lse_part, stream);
+    if (cu) {
+        const size_t cb = static_cast<size_t>(B + 1) * 4;
+        if (overlap(o_part, opb, cu, cb) || overlap(lse_part, lpb, cu, cb)) return FA_ERR_ALIAS;
+    }
+    return splitkv_launch(q, k, v, o, lse, cu, B, H, N, d, scale, causal, num_splits, o_part, lse_part, stream);
+}
+
+int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                   int N, int d, float scale, int causal, int num_splits, float *o_part,
+                   float *lse_part, hipStream_t stream) {
+    return splitkv_ws(q, k, v, o, lse, nullptr, B, H, N, d, scale, causal, num_splits, o_part, lse_part, stream);
+}
+
+int fa_fwd_splitkv_packed(const void *q, const void *k, const void *v, void *o, float *lse,
+                          const int32_t *cu_seqlens, int B, int H, int T, int d, float scale, int causal,
+                          int num_splits, float *o_part, float *lse_part, hipStream_t stream) {
+    if (!cu_seqlens) return FA_ERR_NULLPTR;
+    return splitkv_ws(q, k, v, o, lse, cu_seqlens, B, H, T, d, scale, causal, num_splits, o_part, lse_part,
+                      stream);
 }
 
 int fa_fwd_splitkv_static(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
                           int N, int d, float scale, int causal, int num_splits, hipStream_t stream) {
-    const int rc = splitkv_check(q, k, v, o, lse, B, H, N, d, scale, num_splits);
+    const int rc = splitkv_check(q, k, v, o, lse, nullptr, B, H, N, d, scale, num_splits);
     if (rc != FA_OK) return rc;
     // partials: o_part [S, B, N, H, d] then lse_part [S, B, H, N], fp32;
     // rows * d * 4 is a multiple of 256, so lse_part stays aligned
@@ -325,7 +355,8 @@ int fa_fwd_splitkv_static(const void *q, const void *k, const void *v, void *o, 
     if (sc != FA_OK) return sc;
     float *o_part = static_cast<float *>(base);
     float *lse_part = o_part + static_cast<long long>(num_splits) * rows * d;
-    return splitkv_launch(q, k, v, o, lse, B, H, N, d, scale, causal, num_splits, o_part, lse_part, stream);
+    return splitkv_launch(q, k, v, o, lse, nullptr, B, H, N, d, scale, causal, num_splits, o_part, lse_part,
+                          stream);
 }
 
 long long fa_bwd_workspace_floats(int B, int H, int N) {
@@ -399,16 +430,19 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const flo
     return FA_OK;
 }
 
-int fa_fwd_masked(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N, int d,
-                  float scale, int window_left, int window_right, const float *alibi_slopes, hipStream_t stream) {
+// Masked forward, dense (cu_seqlens == nullptr) or packed (N = T tokens).
+static int masked_impl(const void *q, const void *k, const void *v, void *o, float *lse, const int32_t *cu_seqlens,
+                       int B, int H, int N, int d, float scale, int window_left, int window_right,
+                       const float *alibi_slopes, hipStream_t stream) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULLPTR;
     if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
     if (d != 64 && d != 128 && d != 256) return FA_ERR_HEAD_DIM;
     if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_SCALE;
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) || misaligned(lse, 4) ||
-        misaligned(alibi_slopes, 4))
+        misaligned(alibi_slopes, 4) || misaligned(cu_seqlens, 4))
         return FA_ERR_ALIGN;
-    const long long rows = static_cast<long long>(B) * N * H;
+    const bool packed = cu_seqlens != nullptr;
+    const long long rows = packed ? static_cast<long long>(N) * H : static_cast<long long>(B) * N * H;
     const long long elems = rows * d;
     // window edges are added to row and key indices in 32-bit arithmetic
     if (elems <= 0 || elems > (1LL << 46) || !token_stride_ok(H, d) || N > kMaskedMaxN) return FA_ERR_SHAPE;
@@ -419,6 +453,10 @@ int fa_fwd_masked(const void *q, const void *k, const void *v, void *o, float *l
         if (overlap(o, tb, in, tb) || overlap(lse, lb, in, tb)) return FA_ERR_ALIAS;
     if (overlap(o, tb, lse, lb)) return FA_ERR_ALIAS;
     if (alibi_slopes && (overlap(o, tb, alibi_slopes, sb) || overlap(lse, lb, alibi_slopes, sb))) return FA_ERR_ALIAS;
+    if (packed) {
+        const size_t cb = static_cast<size_t>(B + 1) * 4;
+        if (overlap(o, tb, cu_seqlens, cb) || overlap(lse, lb, cu_seqlens, cb)) return FA_ERR_ALIAS;
+    }
 
     Params prm{};
     prm.q = static_cast<const uint16_t *>(q);
@@ -426,12 +464,14 @@ int fa_fwd_masked(const void *q, const void *k, const void *v, void *o, float *l
     prm.v = static_cast<const uint16_t *>(v);
     prm.o = static_cast<uint16_t *>(o);
     prm.lse = lse;
+    prm.cu = cu_seqlens;
     prm.B = B;
     prm.H = H;
     prm.N = N;
     prm.cs = scale * kLog2e;
-    // an edge at N - 1 or beyond hides no key: clamp it there, so that the
-    // kernel's index arithmetic (row + edge) stays far from overflow
+    // an edge at N - 1 or beyond hides no key (packed: no sequence is longer
+    // than T = N): clamp it there, so that the kernel's index arithmetic
+    // (row + edge) stays far from overflow
     prm.wl = window_left < 0 ? -1 : (window_left < N ? window_left : N - 1);
     prm.wr = window_right < 0 ? -1 : (window_right < N ? window_right : N - 1);
     prm.alibi = alibi_slopes;
@@ -439,12 +479,28 @@ int fa_fwd_masked(const void *q, const void *k, const void *v, void *o, float *l
     const int rows_per_tile = tile_rows_for(d);
     const long long n_qt = (static_cast<long long>(N) + rows_per_tile - 1) / rows_per_tile;
     prm.n_qt = static_cast<int>(n_qt);
-    const long long grid = static_cast<long long>(B) * H * n_qt;
+    // packed: a bound on sum_b ceil(n_b / rows), surplus workgroups exit
+    const long long grid = packed ? static_cast<long long>(H) * (n_qt + B) : static_cast<long long>(B) * H * n_qt;
     if (grid <= 0 || grid > 0x7fffffffLL) return FA_ERR_SHAPE;
-    const KernelFn fn = d == 64 ? select_mods_d64() : (d == 128 ? select_mods_d128() : select_mods_d256());
+    const KernelFn fn = d == 64    ? select_mods_d64(packed)
+                        : d == 128 ? select_mods_d128(packed)
+                                   : select_mods_d256(packed);
     (void)hipGetLastError();
     hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(grid)), dim3(waves_for(d) * 64), 0, stream, prm);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_masked(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N, int d,
+                  float scale, int window_left, int window_right, const float *alibi_slopes, hipStream_t stream) {
+    return masked_impl(q, k, v, o, lse, nullptr, B, H, N, d, scale, window_left, window_right, alibi_slopes, stream);
+}
+
+int fa_fwd_masked_packed(const void *q, const void *k, const void *v, void *o, float *lse,
+                         const int32_t *cu_seqlens, int B, int H, int T, int d, float scale, int window_left,
+                         int window_right, const float *alibi_slopes, hipStream_t stream) {
+    if (!cu_seqlens) return FA_ERR_NULLPTR;
+    return masked_impl(q, k, v, o, lse, cu_seqlens, B, H, T, d, scale, window_left, window_right, alibi_slopes,
+                       stream);
 }
 
 int fa_fp8_vt_stride(int N) { return N < 1 ? 0 : (N + 63) / 64 * 64; }

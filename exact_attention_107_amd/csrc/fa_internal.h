@@ -82,14 +82,14 @@ KernelFn select_count_d128(bool causal, bool varlen, int rescale_mode);
 // The default forward (hardware exp2, strict rescale) with the two halves of
 // the eight-wave workgroup run half a key tile apart (head dimension 128).
 KernelFn select_ping_d128(bool causal, bool varlen);
-// Window-mask / linear-bias instance (dense layout).
-KernelFn select_mods_d64();
-KernelFn select_mods_d128();
-KernelFn select_mods_d256();
-// Split-KV instance (dense layout, partial results into Params::op / lp).
-KernelFn select_split_d64(bool causal);
-KernelFn select_split_d128(bool causal);
-KernelFn select_split_d256(bool causal);
+// Window-mask / linear-bias instance (dense or packed layout).
+KernelFn select_mods_d64(bool varlen);
+KernelFn select_mods_d128(bool varlen);
+KernelFn select_mods_d256(bool varlen);
+// Split-KV instance (dense or packed layout, partial results into Params::op / lp).
+KernelFn select_split_d64(bool causal, bool varlen);
+KernelFn select_split_d128(bool causal, bool varlen);
+KernelFn select_split_d256(bool causal, bool varlen);
 
 // Merge of split-KV partials (fa_merge.hip).
 struct MergeParams {

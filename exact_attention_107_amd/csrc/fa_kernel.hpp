@@ -235,9 +235,9 @@ struct Work {
 
 template <bool CAUSAL, bool VARLEN, int BR, bool SPLIT, bool MODS = false>
 __device__ __forceinline__ bool decode_work(const Params &p, Work &w) {
-    const int wg = blockIdx.x;
+    int wg = blockIdx.x;
     w.split = 0;
-    if constexpr (SPLIT) {
+    if constexpr (SPLIT && !VARLEN) {
         // Items are (b, h, key range, query tile); the ranges of one query
         // tile hold equal work.  Causal: highest query tile first (it sees the
         // most keys).  Non-causal: each XCD
@@ -294,6 +294,12 @@ __device__ __forceinline__ bool decode_work(const Params &p, Work &w) {
         w.t0 = static_cast<long long>(w.b) * p.N;
         return true;
     } else {
+        // packed with key ranges: the ranges of one (sequence, head, query
+        // tile) are consecutive workgroups, the item order below for the rest
+        if constexpr (SPLIT) {
+            w.split = wg % p.nsplit;
+            wg /= p.nsplit;
+        }
         const int lane = threadIdx.x & 63;
         w.h = wg % p.H;
         int r = wg / p.H;
@@ -1049,7 +1055,9 @@ fa_fwd_kernel(Params p) {
         const float inv = lb > 0.0f ? 1.0f / lb : 0.0f;
         if constexpr (SPLIT) {
             // normalised fp32 partial O of this key range, and its LSE
-            const long long sbase = static_cast<long long>(w.split) * p.B * p.N * p.H * D + base;
+            // ([S, tokens, H, D] and [S, B, H, N], packed [S, H, T])
+            const long long tokens = VARLEN ? static_cast<long long>(p.N) : static_cast<long long>(p.B) * p.N;
+            const long long sbase = static_cast<long long>(w.split) * tokens * p.H * D + base;
             const auto prs = make_rsrc(p.op + sbase + rowb * rs, (long long)(n - rowb) * rs * 4);
             const int voff_p = c * static_cast<int>(rs) * 4;
 #pragma unroll
@@ -1066,8 +1074,14 @@ fa_fwd_kernel(Params p) {
             const int qrow = rowb + c;
             if (qrow < n && hh == 0) {
                 const float lse = l > 0.0f ? (m_run[b] + log2f(l)) * kLn2 : -INFINITY;
-                p.lp[(static_cast<long long>(w.split) * p.B * p.H + static_cast<long long>(w.b) * p.H + w.h) *
-                         p.N + qrow] = lse;
+                long long li;
+                if constexpr (VARLEN) {
+                    li = (static_cast<long long>(w.split) * p.H + w.h) * p.N + w.t0 + qrow;
+                } else {
+                    li = (static_cast<long long>(w.split) * p.B * p.H + static_cast<long long>(w.b) * p.H + w.h) *
+                             p.N + qrow;
+                }
+                p.lp[li] = lse;
             }
             continue;
         }
@@ -1143,14 +1157,19 @@ KernelFn select_ping(bool causal, bool varlen) {
 }
 
 template <int D>
-KernelFn select_mods() {
+KernelFn select_mods(bool varlen) {
     constexpr int BC = kTileKeys, NW = Geometry<D>::kWaves, QB = Geometry<D>::kBlocks;
+    if (varlen) return fa_fwd_kernel<D, BC, NW, QB, false, true, FA_EXP_HW, FA_RESCALE_THRESHOLD, false, true>;
     return fa_fwd_kernel<D, BC, NW, QB, false, false, FA_EXP_HW, FA_RESCALE_THRESHOLD, false, true>;
 }
 
 template <int D>
-KernelFn select_split(bool causal) {
+KernelFn select_split(bool causal, bool varlen) {
     constexpr int BC = kTileKeys, NW = Geometry<D>::kWaves, QB = Geometry<D>::kBlocks;
+    if (varlen) {
+        if (causal) return fa_fwd_kernel<D, BC, NW, QB, true, true, FA_EXP_HW, FA_RESCALE_THRESHOLD, true>;
+        return fa_fwd_kernel<D, BC, NW, QB, false, true, FA_EXP_HW, FA_RESCALE_THRESHOLD, true>;
+    }
     if (causal) return fa_fwd_kernel<D, BC, NW, QB, true, false, FA_EXP_HW, FA_RESCALE_THRESHOLD, true>;
     return fa_fwd_kernel<D, BC, NW, QB, false, false, FA_EXP_HW, FA_RESCALE_THRESHOLD, true>;
 }

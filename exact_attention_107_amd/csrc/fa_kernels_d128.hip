@@ -7,9 +7,9 @@ KernelFn select_d128(bool causal, bool varlen, int exp_mode, int rescale_mode) {
     return select_kernel<128>(causal, varlen, exp_mode, rescale_mode);
 }
 
-KernelFn select_split_d128(bool causal) { return select_split<128>(causal); }
+KernelFn select_split_d128(bool causal, bool varlen) { return select_split<128>(causal, varlen); }
 
-KernelFn select_mods_d128() { return select_mods<128>(); }
+KernelFn select_mods_d128(bool varlen) { return select_mods<128>(varlen); }
 
 KernelFn select_count_d128(bool causal, bool varlen, int rescale_mode) {
     return select_count<128>(causal, varlen, rescale_mode);

@@ -23,7 +23,8 @@ EXPORTS = ("fa_fwd", "fa_fwd_variant", "fa_strerror", "fa_tile_rows", "fa_tile_k
            "fa_fwd_splitkv", "fa_merge", "fa_split_range", "fa_num_splits", "fa_bwd",
            "fa_bwd_workspace_floats", "fa_fwd_fp8", "fa_quantize_fp8", "fa_fp8_vt_stride",
            "fa_fwd_masked", "fa_fwd_rescale_counts", "fa_fwd_splitkv_static", "fa_fwd_pingpong",
-           "fa_fp8_vt_stride_packed", "fa_quantize_fp8_packed", "fa_fwd_fp8_packed")
+           "fa_fp8_vt_stride_packed", "fa_quantize_fp8_packed", "fa_fwd_fp8_packed", "fa_fwd_splitkv_packed",
+           "fa_fwd_masked_packed")
 FA_ERR_SCRATCH = 10
 STATIC_SCRATCH_BYTES = 64 << 20   # FA_STATIC_SCRATCH_BYTES of include/fa.h
 
@@ -85,6 +86,10 @@ def load(path: str | None = None):
     lib.fa_quantize_fp8_packed.restype = i32
     lib.fa_fwd_fp8_packed.argtypes = [vp] * 9 + [i32, i32, i32, i32, ctypes.c_float, i32, vp]
     lib.fa_fwd_fp8_packed.restype = i32
+    lib.fa_fwd_splitkv_packed.argtypes = [vp] * 6 + [i32, i32, i32, i32, ctypes.c_float, i32, i32, vp, vp, vp]
+    lib.fa_fwd_splitkv_packed.restype = i32
+    lib.fa_fwd_masked_packed.argtypes = [vp] * 6 + [i32, i32, i32, i32, ctypes.c_float, i32, i32, vp, vp]
+    lib.fa_fwd_masked_packed.restype = i32
     lib.fa_fwd_masked.argtypes = [vp] * 5 + [i32, i32, i32, i32, ctypes.c_float, i32, i32, vp, vp]
     lib.fa_fwd_masked.restype = i32
     lib.fa_fwd_pingpong.argtypes = common
@@ -288,6 +293,86 @@ def fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bo
         rc = lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                 B, H, N, d, ctypes.c_float(scale), int(bool(causal)), S,
                                 o_part.data_ptr(), lse_part.data_ptr(), ctypes.c_void_p(s.cuda_stream))
+    if rc != 0:
+        raise FaError(rc, strerror(rc))
+    return out, lse
+
+
+def _packed_qkv(q, k, v, cu_seqlens):
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a GPU tensor")
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, name, torch.bfloat16, dev)
+    if k.shape != q.shape or v.shape != q.shape or q.dim() != 3:
+        raise ValueError("packed q, k and v must be [T, H, d] of one shape")
+    B = _packed_cu(cu_seqlens, dev)
+    T, H, d = (int(x) for x in q.shape)
+    return dev, B, T, H, d
+
+
+def fwd_splitkv_packed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor, *,
+                       splits: int, causal: bool = False, scale: float | None = None,
+                       out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                       o_part: torch.Tensor | None = None, lse_part: torch.Tensor | None = None,
+                       stream: torch.cuda.Stream | None = None):
+    """Split-KV forward over packed sequences (``fa_fwd_splitkv_packed``):
+    ``q, k, v [T, H, d]``, ``cu_seqlens`` int32 ``[B+1]``; the fp32
+    workspaces ``o_part [S, T, H, d]`` and ``lse_part [S, H, T]`` are
+    allocated with torch unless given.  Returns ``(o [T, H, d], lse [H, T])``."""
+    lib = load()
+    dev, B, T, H, d = _packed_qkv(q, k, v, cu_seqlens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    S = int(splits)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((H, T), dtype=torch.float32, device=dev) if lse is None else lse
+    o_part = torch.empty((S, T, H, d), dtype=torch.float32, device=dev) if o_part is None else o_part
+    lse_part = torch.empty((S, H, T), dtype=torch.float32, device=dev) if lse_part is None else lse_part
+    for t, name, dt, shape in ((out, "out", torch.bfloat16, (T, H, d)), (lse, "lse", torch.float32, (H, T)),
+                               (o_part, "o_part", torch.float32, (S, T, H, d)),
+                               (lse_part, "lse_part", torch.float32, (S, H, T))):
+        _check(t, name, dt, dev)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be {shape}")
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = lib.fa_fwd_splitkv_packed(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                       cu_seqlens.data_ptr(), B, H, T, d, ctypes.c_float(scale), int(bool(causal)),
+                                       S, o_part.data_ptr(), lse_part.data_ptr(), ctypes.c_void_p(s.cuda_stream))
+    if rc != 0:
+        raise FaError(rc, strerror(rc))
+    return out, lse
+
+
+def fwd_masked_packed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor, *,
+                      window_left: int = -1, window_right: int = -1, alibi_slopes: torch.Tensor | None = None,
+                      scale: float | None = None, out: torch.Tensor | None = None,
+                      lse: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None):
+    """Window mask and ALiBi over packed sequences (``fa_fwd_masked_packed``):
+    positions count from each sequence's first token.  Returns
+    ``(o [T, H, d], lse [H, T])``."""
+    lib = load()
+    dev, B, T, H, d = _packed_qkv(q, k, v, cu_seqlens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if alibi_slopes is not None:
+        _check(alibi_slopes, "alibi_slopes", torch.float32, dev)
+        if tuple(alibi_slopes.shape) != (H,):
+            raise ValueError(f"alibi_slopes must be ({H},)")
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((H, T), dtype=torch.float32, device=dev) if lse is None else lse
+    _check(out, "out", torch.bfloat16, dev)
+    _check(lse, "lse", torch.float32, dev)
+    if tuple(out.shape) != (T, H, d) or tuple(lse.shape) != (H, T):
+        raise ValueError(f"out must be {(T, H, d)} and lse {(H, T)}")
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = lib.fa_fwd_masked_packed(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                      cu_seqlens.data_ptr(), B, H, T, d, ctypes.c_float(scale), int(window_left),
+                                      int(window_right),
+                                      None if alibi_slopes is None else alibi_slopes.data_ptr(),
+                                      ctypes.c_void_p(s.cuda_stream))
     if rc != 0:
         raise FaError(rc, strerror(rc))
     return out, lse

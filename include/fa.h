@@ -151,7 +151,7 @@ int fa_fwd_pingpong(const void *q, const void *k, const void *v, void *o,
                     int causal, const int32_t *cu_seqlens, hipStream_t stream);
 
 /*
- * Split-KV forward (dense layout only).  For every (b, h) and query tile of
+ * Split-KV forward (dense layout; packed: fa_fwd_splitkv_packed).  For every (b, h) and query tile of
  * fa_tile_rows(d) rows, the keys that tile sees (all N, or when causal those
  * up to its last row) are cut into num_splits consecutive ranges of whole
  * K/V tiles of near-equal length: with T such tiles, range s holds tiles
@@ -183,6 +183,28 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o,
                    float *lse, int B, int H, int N, int d, float scale,
                    int causal, int num_splits, float *o_part, float *lse_part,
                    hipStream_t stream);
+
+/*
+ * fa_fwd_splitkv_packed: fa_fwd_splitkv over packed sequences (the packed
+ * layout of fa_fwd: q, k, v, o [T, H, d], lse [H, T], cu_seqlens device int32
+ * [B + 1]; variable-length sequences are a case of the tile scheduler in
+ * section 3.4 of "Understanding FlashAttention V4").  Each sequence's query
+ * tiles are cut into key ranges as fa_fwd_splitkv cuts a dense sequence of
+ * its length (fa_split_range with N = that length): a short sequence's
+ * ranges past its last key tile are empty.
+ *   num_splits  1 .. ceil(T / fa_tile_keys(d)).
+ *   o_part      device fp32 workspace [num_splits, T, H, d].
+ *   lse_part    device fp32 workspace [num_splits, H, T].
+ * Each sequence's O and LSE are bitwise those of fa_fwd_splitkv on that
+ * sequence alone with min(num_splits, ceil(n / fa_tile_keys(d))) ranges.
+ * Errors as fa_fwd_splitkv;
+ * FA_ERR_NULLPTR for cu_seqlens == NULL.
+ */
+int fa_fwd_splitkv_packed(const void *q, const void *k, const void *v, void *o,
+                          float *lse, const int32_t *cu_seqlens, int B, int H,
+                          int T, int d, float scale, int causal,
+                          int num_splits, float *o_part, float *lse_part,
+                          hipStream_t stream);
 
 /* Size of the static scratch of fa_fwd_splitkv_static, per GPU: 64 MiB. */
 #define FA_STATIC_SCRATCH_BYTES (64u << 20)
@@ -327,6 +349,20 @@ int fa_fwd_masked(const void *q, const void *k, const void *v, void *o,
                   float *lse, int B, int H, int N, int d, float scale,
                   int window_left, int window_right, const float *alibi_slopes,
                   hipStream_t stream);
+
+/*
+ * fa_fwd_masked_packed: fa_fwd_masked over packed sequences (q, k, v, o
+ * [T, H, d], lse [H, T], cu_seqlens device int32 [B + 1] as fa_fwd).  Row
+ * and key positions i, j count from each sequence's first token, and a
+ * query sees only its own sequence's keys; the window and the bias are
+ * otherwise as fa_fwd_masked's.  T <= 2^30.  Errors as fa_fwd_masked;
+ * FA_ERR_NULLPTR for cu_seqlens == NULL.
+ */
+int fa_fwd_masked_packed(const void *q, const void *k, const void *v, void *o,
+                         float *lse, const int32_t *cu_seqlens, int B, int H,
+                         int T, int d, float scale, int window_left,
+                         int window_right, const float *alibi_slopes,
+                         hipStream_t stream);
 
 /*
  * FP8 forward (dense layout, d = 64, 128 or 256).  The FlashAttention-3 notes of

@@ -403,3 +403,40 @@ def test_fp8_packed_binding_checks_shapes():
     with pytest.raises(ValueError, match="out must be"):
         fa.quantize_fp8_packed(torch.zeros(T, H, d, dtype=torch.bfloat16), cu,
                                out=torch.empty(T, H, d - 1, dtype=torch.uint8))
+
+
+# ---------------------------------------------------------------------------
+# Split-KV and masks over packed sequences
+
+def call_split_p(lib, q=Q, k=K, v=V, o=O, lse=L, cu=CU8, B=2, H=2, T=1000, d=128, scale=0.125, causal=0,
+                 splits=4, op=OP, lp=LP):
+    return lib.fa_fwd_splitkv_packed(*(ctypes.c_void_p(a) if a else None for a in (q, k, v, o, lse, cu)), B, H, T, d,
+                                     ctypes.c_float(scale), causal, splits,
+                                     *(ctypes.c_void_p(a) if a else None for a in (op, lp)), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=0), NULLPTR), (dict(op=0), NULLPTR), (dict(T=0), SHAPE), (dict(d=96), HEAD_DIM),
+    (dict(scale=0.0), SCALE), (dict(splits=0), SPLIT), (dict(splits=17), SPLIT), (dict(cu=CU8 + 2), ALIGN),
+    (dict(op=OP + 4), ALIGN), (dict(o=Q), ALIAS), (dict(lp=CU8), ALIAS), (dict(o=CU8 - 64), ALIAS),
+    (dict(op=O), ALIAS),
+])
+def test_splitkv_packed_invalid_arguments_are_rejected(lib, kw, code):
+    assert call_split_p(lib, **kw) == code
+
+
+def call_masked_p(lib, q=Q, k=K, v=V, o=O, lse=L, cu=CU8, B=2, H=2, T=100, d=128, scale=0.125, wl=-1, wr=0,
+                  alibi=None):
+    return lib.fa_fwd_masked_packed(*(ctypes.c_void_p(a) if a else None for a in (q, k, v, o, lse, cu)), B, H, T, d,
+                                    ctypes.c_float(scale), wl, wr, None if alibi is None else ctypes.c_void_p(alibi),
+                                    None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=0), NULLPTR), (dict(lse=0), NULLPTR), (dict(T=0), SHAPE), (dict(B=0), SHAPE), (dict(d=96), HEAD_DIM),
+    (dict(scale=float("nan")), SCALE), (dict(cu=CU8 + 1), ALIGN), (dict(alibi=0x700002), ALIGN),
+    (dict(o=V), ALIAS), (dict(lse=CU8), ALIAS),
+    (dict(B=1, H=1, d=64, T=(1 << 30) + 1, q=1 << 40, k=2 << 40, v=3 << 40, o=4 << 40, lse=5 << 40), SHAPE),
+])
+def test_masked_packed_invalid_arguments_are_rejected(lib, kw, code):
+    assert call_masked_p(lib, **kw) == code

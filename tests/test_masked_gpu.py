@@ -93,3 +93,67 @@ def test_masked_huge_window_edges_mean_unbounded(d):
         assert torch.equal(lse, r[1]), (left, right)
     ro, rl = omods.attention(inp["q"], inp["k"], inp["v"], scale=inp["scale"], left=-1, right=-1, slopes=None)
     assert_within(metrics(from_dev(ref[0]), ref[1].cpu().numpy(), ro, rl), "unbounded window")
+
+
+# ---------------------------------------------------------------------------
+# Packed sequences (cu_seqlens): positions count from each sequence's start.
+
+PACKED_LENGTHS = [1, 0, 5, 130, 257, 64, 300, 33]
+
+
+def _packed(lengths, d, H=3, seed=94):
+    return make_inputs(Run("mkp", len(lengths), H, 0, d, False, seed, varlen=True), lengths=lengths)
+
+
+def _run_packed(inp, left, right, slopes):
+    q, k, v = (to_dev(inp[x]) for x in ("q", "k", "v"))
+    cu = torch.from_numpy(np.asarray(inp["cu_seqlens"], dtype=np.int32)).cuda()
+    sl = torch.from_numpy(slopes).cuda() if slopes is not None else None
+    o, lse = fa.fwd_masked_packed(q, k, v, cu, window_left=left, window_right=right, alibi_slopes=sl,
+                                  scale=inp["scale"])
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("window", [(-1, 0), (100, 37), (0, 0), (-1, -1), (63, 64)], ids=lambda w: f"{w[0]}_{w[1]}")
+@pytest.mark.parametrize("bias", [False, True])
+def test_masked_packed_small(d, window, bias):
+    """Empty, one-token and ragged sequences, every element."""
+    inp = _packed(PACKED_LENGTHS, d)
+    slopes = _alibi(3) if bias else None
+    o, lse = _run_packed(inp, *window, slopes)
+    ro, rl = omods.attention_packed(inp["q"], inp["k"], inp["v"], inp["cu_seqlens"], scale=inp["scale"],
+                                    left=window[0], right=window[1], slopes=slopes)
+    m = metrics(from_dev(o), lse.cpu().numpy(), ro, rl)
+    print(f"packed d={d} window={window} bias={bias} {m}")
+    assert_within(m, f"packed window={window} bias={bias}")
+
+
+def test_masked_packed_equals_dense_bitwise():
+    """Each packed sequence gives bitwise the output of a dense masked run of
+    it alone."""
+    lengths = [37, 300, 129, 64]
+    inp = _packed(lengths, 128, H=2, seed=95)
+    slopes = _alibi(2)
+    o, lse = _run_packed(inp, 40, 5, slopes)
+    cu = inp["cu_seqlens"]
+    for b, n in enumerate(lengths):
+        t0 = int(cu[b])
+        one = {x: inp[x][None, t0:t0 + n] for x in ("q", "k", "v")}
+        one["scale"] = inp["scale"]
+        od, ld = _run(one, 40, 5, slopes)
+        assert torch.equal(o[t0:t0 + n].view(torch.int16), od[0].view(torch.int16)), b
+        assert torch.equal(lse[:, t0:t0 + n], ld[0]), b
+
+
+def test_masked_packed_many_sequences():
+    """More than 64 sequences (the decode walks them 64 at a time)."""
+    rng = np.random.default_rng(96)
+    lengths = [int(x) for x in rng.integers(0, 160, size=150)]
+    inp = _packed(lengths, 64, H=2, seed=97)
+    slopes = _alibi(2)
+    o, lse = _run_packed(inp, 20, 0, slopes)
+    ro, rl = omods.attention_packed(inp["q"], inp["k"], inp["v"], inp["cu_seqlens"], scale=inp["scale"],
+                                    left=20, right=0, slopes=slopes)
+    assert_within(metrics(from_dev(o), lse.cpu().numpy(), ro, rl), "150 sequences")

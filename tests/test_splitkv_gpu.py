@@ -175,3 +175,79 @@ def test_splitkv_full_size_sampled(name):
     assert_within(m, name)
     # every row's LSE is finite and O is finite
     assert torch.isfinite(lse).all() and torch.isfinite(o.float()).all()
+
+
+# ---------------------------------------------------------------------------
+# Packed sequences (cu_seqlens): each sequence's query tiles are cut into key
+# ranges as a dense sequence of its length would be.
+
+PACKED_LENGTHS = [1, 0, 5, 130, 257, 64, 300, 33, 1000]
+
+
+def _packed_inputs(lengths, d, causal, H=3, seed=97):
+    return make_inputs(Run("split_p", len(lengths), H, 0, d, causal, seed, varlen=True), lengths=lengths)
+
+
+def _run_packed(inp, splits):
+    q, k, v = (to_dev(inp[x]) for x in ("q", "k", "v"))
+    cu = torch.from_numpy(np.asarray(inp["cu_seqlens"], dtype=np.int32)).cuda()
+    T, H, d = inp["q"].shape
+    o_part = torch.empty((splits, T, H, d), dtype=torch.float32, device="cuda")
+    lse_part = torch.empty((splits, H, T), dtype=torch.float32, device="cuda")
+    o, lse = fa.fwd_splitkv_packed(q, k, v, cu, splits=splits, causal=inp["causal"], scale=inp["scale"],
+                                   o_part=o_part, lse_part=lse_part)
+    torch.cuda.synchronize()
+    return o, lse, o_part, lse_part
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("splits", [1, 3, 16])
+def test_splitkv_packed_small(d, causal, splits):
+    """Empty, one-token, ragged and long sequences in one batch (16 ranges:
+    most sequences have fewer key tiles, so most of their ranges are empty);
+    every element of O and LSE."""
+    inp = _packed_inputs(PACKED_LENGTHS, d, causal)
+    o, lse, _, _ = _run_packed(inp, splits)
+    o_ref, lse_ref = oracle.attention(inp["q"], inp["k"], inp["v"], scale=inp["scale"], causal=causal,
+                                      cu_seqlens=inp["cu_seqlens"])
+    m = metrics(from_dev(o), lse.cpu().numpy(), o_ref, lse_ref)
+    print(f"packed split d={d} causal={causal} S={splits} {m}")
+    assert_within(m, f"packed split d={d} causal={causal} S={splits}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_splitkv_packed_equals_dense_bitwise(causal):
+    """Each packed sequence's O and LSE are bitwise those of the dense
+    split-KV forward on that sequence alone with min(S, its key tiles)
+    ranges (with more ranges than key tiles every non-empty range is one
+    tile, and empty ranges add exact zeros in the merge); with S ranges, its
+    partials are bitwise the dense ones too."""
+    lengths = [37, 300, 129, 1000]
+    S = 5
+    inp = _packed_inputs(lengths, 128, causal, H=2, seed=98)
+    o, lse, op, lp = _run_packed(inp, S)
+    cu = inp["cu_seqlens"]
+    for b, n in enumerate(lengths):
+        t0 = int(cu[b])
+        one = {x: inp[x][None, t0:t0 + n] for x in ("q", "k", "v")}
+        one.update(causal=causal, scale=inp["scale"])
+        s_dense = min(S, -(-n // 64))
+        od, ld, opd, lpd = _run(one, s_dense)
+        assert torch.equal(o[t0:t0 + n].view(torch.int16), od[0].view(torch.int16)), b
+        assert torch.equal(lse[:, t0:t0 + n], ld[0]), b
+        if s_dense == S:
+            assert torch.equal(op[:, t0:t0 + n], opd[:, 0]), b
+            assert torch.equal(lp[:, :, t0:t0 + n], lpd[:, 0]), b
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_splitkv_packed_many_sequences(causal):
+    """More than 64 sequences (the decode walks them 64 at a time)."""
+    rng = np.random.default_rng(99)
+    lengths = [int(x) for x in rng.integers(0, 300, size=150)]
+    inp = _packed_inputs(lengths, 64, causal, H=2, seed=100)
+    o, lse, _, _ = _run_packed(inp, 3)
+    o_ref, lse_ref = oracle.attention(inp["q"], inp["k"], inp["v"], scale=inp["scale"], causal=causal,
+                                      cu_seqlens=inp["cu_seqlens"])
+    assert_within(metrics(from_dev(o), lse.cpu().numpy(), o_ref, lse_ref), f"150 sequences causal={causal}")
