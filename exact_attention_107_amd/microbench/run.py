@@ -1,12 +1,13 @@
 """Build and run the gfx950 issue-rate microbenchmarks of this directory.
 
-    python exact_attention_107_amd/microbench/run.py [co_issue] [lds_read] ...
+    python exact_attention_107_amd/microbench/run.py [co_issue] [fp8_acc] [lds_read] ...
 
 Each probe is a stand-alone HIP program (hipcc, gfx950, the library's
 compile flags) built into a temporary directory and run once; its table is
 printed as is.  The probes measure the limits the forward kernel's design
 rests on: how MFMA and VALU instructions share a SIMD, the issue cost of the
-softmax's VALU instructions, and LDS read bandwidth.
+softmax's VALU instructions, LDS read bandwidth, and the accumulation error
+of the FP8 matrix product (which sets the FP8 forward's error bound).
 """
 from __future__ import annotations
 
