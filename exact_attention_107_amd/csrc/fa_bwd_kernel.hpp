@@ -223,11 +223,11 @@ __device__ __forceinline__ bool bwd_packed_item(const BwdParams &p, BwdItem &it)
         // lane b: where sequence b's tiles start when longer sequences (ties:
         // lower index) come first
         const int b = lane;
-        const int len = b < p.B ? p.cu[b + 1] - p.cu[b] : 0;
+        const int len = b < p.B ? seq_len(p.cu, b, p.N) : 0;
         const int tiles = (len + TILE - 1) / TILE;
         int pos = 0;
         for (int o = 0; o < p.B; ++o) {
-            const int lo = p.cu[o + 1] - p.cu[o];
+            const int lo = seq_len(p.cu, o, p.N);
             pos += (lo > len || (lo == len && o < b)) ? (lo + TILE - 1) / TILE : 0;
         }
         const unsigned long long m = __ballot(b < p.B && r >= pos && r < pos + tiles);
@@ -239,7 +239,7 @@ __device__ __forceinline__ bool bwd_packed_item(const BwdParams &p, BwdItem &it)
         int pos = 0;  // tiles of the sequences before this chunk of 64
         for (int c0 = 0; c0 < p.B; c0 += 64) {
             const int b = c0 + lane;
-            const int tiles = b < p.B ? (p.cu[b + 1] - p.cu[b] + TILE - 1) / TILE : 0;
+            const int tiles = b < p.B ? (seq_len(p.cu, b, p.N) + TILE - 1) / TILE : 0;
             int incl = tiles;  // inclusive prefix sum over the lanes
             for (int off = 1; off < 64; off <<= 1) {
                 const int x = __shfl_up(incl, off);
@@ -259,8 +259,10 @@ __device__ __forceinline__ bool bwd_packed_item(const BwdParams &p, BwdItem &it)
         if (sel < 0) return false;
     }
     it.tile = HIGH_FIRST ? tiles_sel - 1 - local : local;
-    const int s0 = __builtin_amdgcn_readfirstlane(p.cu[sel]);
-    const int s1 = __builtin_amdgcn_readfirstlane(p.cu[sel + 1]);
+    int s0, s1;
+    seq_span(p.cu, sel, p.N, s0, s1);
+    s0 = __builtin_amdgcn_readfirstlane(s0);
+    s1 = __builtin_amdgcn_readfirstlane(s1);
     it.t0 = s0;
     it.n = s1 - s0;
     it.lrow = static_cast<long long>(it.h) * p.N + s0;

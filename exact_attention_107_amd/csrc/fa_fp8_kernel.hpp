@@ -61,16 +61,20 @@ __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
 }
 
 // Column of sequence b's first key in a packed V^T row: the sum of
-// ceil(n / 64) * 64 over the sequences before it (the host bounds the total
-// below 2^31), summed 64 sequences at a time by the wave.
-__device__ __forceinline__ int fp8_packed_vt_start(const int32_t *cu, int b) {
+// ceil(n / 64) * 64 over the sequences before it, summed 64 sequences at a
+// time by the wave.  Well-formed offsets keep the sum below the row length
+// vts (the host bounds vts below 2^31); the caller skips a sequence whose
+// padded keys would end past vts (only malformed offsets, e.g. overlapping
+// sequences, get there), and the running sum is capped at vts so it cannot
+// overflow.
+__device__ __forceinline__ int fp8_packed_vt_start(const int32_t *cu, int b, int T, int vts) {
     const int lane = threadIdx.x & 63;
     int s = 0;
     for (int o0 = 0; o0 < b; o0 += 64) {
         const int o = o0 + lane;
-        int v = o < b ? (cu[o + 1] - cu[o] + 63) / 64 * 64 : 0;
+        int v = o < b ? (seq_len(cu, o, T) + 63) / 64 * 64 : 0;
         for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-        s += v;
+        s = min(s + v, vts);
     }
     return __builtin_amdgcn_readfirstlane(s);
 }
@@ -119,7 +123,8 @@ fa_fp8_fwd_kernel(Fp8Params p) {
     long long vspan;
     if constexpr (PACKED) {
         np = p.vts;
-        const int start = fp8_packed_vt_start(p.cu, b);
+        const int start = fp8_packed_vt_start(p.cu, b, p.N, p.vts);
+        if (start + (n + 63) / 64 * 64 > np) return;   // malformed offsets only
         vt = p.vt + static_cast<long long>(h) * D * np + start;
         vspan = static_cast<long long>(D) * np - start;
     } else {
@@ -437,7 +442,9 @@ __global__ void __launch_bounds__(256) fa_fp8_quant_kernel(QuantParams p) {
 __global__ void __launch_bounds__(256) fa_fp8_amax_packed_kernel(QuantParams p) {
     const int bh = blockIdx.x;
     const int b = bh / p.H, h = bh - b * p.H;
-    const int t0 = p.cu[b], n = p.cu[b + 1] - t0;
+    int t0, t1;
+    seq_span(p.cu, b, p.N, t0, t1);
+    const int n = t1 - t0;
     const int chunks = p.d / 8;
     const long long total = static_cast<long long>(n) * chunks;
     float m = 0.0f;
@@ -464,7 +471,9 @@ __global__ void __launch_bounds__(256) fa_fp8_amax_packed_kernel(QuantParams p) 
 __global__ void __launch_bounds__(256) fa_fp8_quant_packed_kernel(QuantParams p) {
     const int bh = blockIdx.x;
     const int b = bh / p.H, h = bh - b * p.H;
-    const int t0 = p.cu[b], n = p.cu[b + 1] - t0;
+    int t0, t1;
+    seq_span(p.cu, b, p.N, t0, t1);
+    const int n = t1 - t0;
     const int q4 = p.d / 4;
     const float inv = 1.0f / p.descale[bh];
     auto codes_of = [&](long long tok, int cq) {
@@ -483,7 +492,8 @@ __global__ void __launch_bounds__(256) fa_fp8_quant_packed_kernel(QuantParams p)
     }
     // transposed: lanes run along the sequence's (padded) keys
     const int pad = (n + 63) / 64 * 64;
-    const int start = fp8_packed_vt_start(p.cu, b);
+    const int start = fp8_packed_vt_start(p.cu, b, p.N, p.vts);
+    if (start + pad > p.vts) return;   // malformed offsets only
     const long long total = static_cast<long long>(pad) * q4;
     for (long long t = threadIdx.x; t < total; t += 256) {
         const int cq = static_cast<int>(t / pad);

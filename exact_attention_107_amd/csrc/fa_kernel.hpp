@@ -225,6 +225,22 @@ __device__ __forceinline__ void static_for(F &&f) {
 }
 
 // ---------------------------------------------------------------------------
+// Packed sequence b spans tokens [s0, s1) of T.  The offsets are read on the
+// device and not validated; clamping them to [0, T] leaves well-formed ones
+// unchanged and turns malformed ones (decreasing, negative, past T) into
+// empty or shortened sequences inside the buffers, never into accesses past
+// them.
+__device__ __forceinline__ void seq_span(const int32_t *cu, int b, int T, int &s0, int &s1) {
+    s0 = min(max(cu[b], 0), T);
+    s1 = min(max(cu[b + 1], s0), T);
+}
+__device__ __forceinline__ int seq_len(const int32_t *cu, int b, int T) {
+    int s0, s1;
+    seq_span(cu, b, T, s0, s1);
+    return s1 - s0;
+}
+
+// ---------------------------------------------------------------------------
 // Work decode: one workgroup = (sequence b, head h, query tile qt).
 
 struct Work {
@@ -310,11 +326,11 @@ __device__ __forceinline__ bool decode_work(const Params &p, Work &w) {
             // about the same time on one XCD (wg % 8) and share its L2.
             // Lane b computes where sequence b's tiles start in that order.
             const int b = lane;
-            const int len = b < p.B ? p.cu[b + 1] - p.cu[b] : 0;
+            const int len = b < p.B ? seq_len(p.cu, b, p.N) : 0;
             const int tiles = (len + BR - 1) / BR;
             int pos = 0;
             for (int o = 0; o < p.B; ++o) {
-                const int lo = p.cu[o + 1] - p.cu[o];
+                const int lo = seq_len(p.cu, o, p.N);
                 const bool before = lo > len || (lo == len && o < b);
                 pos += before ? (lo + BR - 1) / BR : 0;
             }
@@ -326,8 +342,10 @@ __device__ __forceinline__ bool decode_work(const Params &p, Work &w) {
             const int tiles_sel = __builtin_amdgcn_readfirstlane(__shfl(tiles, bsel));
             w.b = bsel;
             w.qt = tiles_sel - 1 - (r - pos_sel);
-            const int s0 = __builtin_amdgcn_readfirstlane(p.cu[bsel]);
-            const int s1 = __builtin_amdgcn_readfirstlane(p.cu[bsel + 1]);
+            int s0, s1;
+            seq_span(p.cu, bsel, p.N, s0, s1);
+            s0 = __builtin_amdgcn_readfirstlane(s0);
+            s1 = __builtin_amdgcn_readfirstlane(s1);
             w.t0 = s0;
             w.n = s1 - s0;
             return true;
@@ -339,7 +357,7 @@ __device__ __forceinline__ bool decode_work(const Params &p, Work &w) {
         for (int base = 0; base < p.B; base += 64) {
             const int b = base + lane;
             int nt = 0;
-            if (b < p.B) nt = (p.cu[b + 1] - p.cu[b] + BR - 1) / BR;
+            if (b < p.B) nt = (seq_len(p.cu, b, p.N) + BR - 1) / BR;
             for (int off = 32; off > 0; off >>= 1) nt = max(nt, __shfl_xor(nt, off));
             lmax = max(lmax, __builtin_amdgcn_readfirstlane(nt));
         }
@@ -348,14 +366,14 @@ __device__ __forceinline__ bool decode_work(const Params &p, Work &w) {
             for (int base = 0; base < p.B; base += 64) {
                 const int b = base + lane;
                 bool on = false;
-                if (b < p.B) on = (p.cu[b + 1] - p.cu[b] + BR - 1) / BR > L;
+                if (b < p.B) on = (seq_len(p.cu, b, p.N) + BR - 1) / BR > L;
                 cnt += __popcll(__ballot(on));
             }
             if (r < cnt) {
                 for (int base = 0; base < p.B; base += 64) {
                     const int b = base + lane;
                     bool on = false;
-                    if (b < p.B) on = (p.cu[b + 1] - p.cu[b] + BR - 1) / BR > L;
+                    if (b < p.B) on = (seq_len(p.cu, b, p.N) + BR - 1) / BR > L;
                     unsigned long long m = __ballot(on);
                     const int c = __popcll(m);
                     if (r < c) {
@@ -366,8 +384,10 @@ __device__ __forceinline__ bool decode_work(const Params &p, Work &w) {
                             base + __ffsll(static_cast<long long>(m)) - 1);
                         w.b = bsel;
                         w.qt = __builtin_amdgcn_readfirstlane(L);
-                        const int s0 = __builtin_amdgcn_readfirstlane(p.cu[bsel]);
-                        const int s1 = __builtin_amdgcn_readfirstlane(p.cu[bsel + 1]);
+                        int s0, s1;
+                        seq_span(p.cu, bsel, p.N, s0, s1);
+                        s0 = __builtin_amdgcn_readfirstlane(s0);
+                        s1 = __builtin_amdgcn_readfirstlane(s1);
                         w.t0 = s0;
                         w.n = s1 - s0;
                         return true;

@@ -30,6 +30,23 @@ STATIC_SCRATCH_BYTES = 64 << 20   # FA_STATIC_SCRATCH_BYTES of include/fa.h
 
 _lib = None
 
+# The library reads cu_seqlens on the device and does not validate its
+# contents (its kernels clamp every sequence to [0, T], so malformed offsets
+# give wrong results, not out-of-range accesses).  With FA_CHECK_CU_SEQLENS=1
+# in the environment every packed call first checks the offsets on the host
+# (a copy and a synchronisation per call: for debugging, not for hot loops).
+CHECK_CU_SEQLENS = os.environ.get("FA_CHECK_CU_SEQLENS", "") not in ("", "0")
+
+
+def check_cu_seqlens(cu_seqlens: torch.Tensor, T: int) -> None:
+    """Raise ValueError unless ``cu_seqlens`` (int32 ``[B+1]``, any device)
+    starts at 0, never decreases and ends at ``T``."""
+    c = cu_seqlens.detach().to("cpu", torch.int64)
+    if c.dim() != 1 or c.numel() < 2:
+        raise ValueError("cu_seqlens must be [B+1]")
+    if int(c[0]) != 0 or int(c[-1]) != int(T) or bool((c[1:] < c[:-1]).any()):
+        raise ValueError(f"cu_seqlens must start at 0, be non-decreasing and end at T = {T}")
+
 
 class FaError(RuntimeError):
     def __init__(self, code: int, msg: str):
@@ -162,6 +179,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
         B = cu_seqlens.numel() - 1
         lse_shape = (H, N)
         cu_ptr = cu_seqlens.data_ptr()
+        if CHECK_CU_SEQLENS:
+            check_cu_seqlens(cu_seqlens, N)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -306,8 +325,8 @@ def _packed_qkv(q, k, v, cu_seqlens):
         _check(t, name, torch.bfloat16, dev)
     if k.shape != q.shape or v.shape != q.shape or q.dim() != 3:
         raise ValueError("packed q, k and v must be [T, H, d] of one shape")
-    B = _packed_cu(cu_seqlens, dev)
     T, H, d = (int(x) for x in q.shape)
+    B = _packed_cu(cu_seqlens, dev, T)
     return dev, B, T, H, d
 
 
@@ -476,6 +495,8 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse:
         N, H, d = q.shape
         B = cu_seqlens.numel() - 1
         lse_shape, ws_batch, cu_ptr = (H, N), 1, cu_seqlens.data_ptr()
+        if CHECK_CU_SEQLENS:
+            check_cu_seqlens(cu_seqlens, N)
     shape = tuple(q.shape)
     for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
         _check(t, name, torch.bfloat16, dev)
@@ -582,10 +603,12 @@ def fp8_vt_stride_packed(T: int, B: int) -> int:
     return int(load().fa_fp8_vt_stride_packed(int(T), int(B)))
 
 
-def _packed_cu(cu_seqlens, dev):
+def _packed_cu(cu_seqlens, dev, T: int):
     _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
     if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
         raise ValueError("cu_seqlens must be int32 [B+1]")
+    if CHECK_CU_SEQLENS:
+        check_cu_seqlens(cu_seqlens, T)
     return cu_seqlens.numel() - 1
 
 
@@ -602,7 +625,7 @@ def quantize_fp8_packed(x: torch.Tensor, cu_seqlens: torch.Tensor, *, transpose:
     if x.dim() != 3:
         raise ValueError("packed x must be [T, H, d]")
     T, H, d = (int(v) for v in x.shape)
-    B = _packed_cu(cu_seqlens, dev)
+    B = _packed_cu(cu_seqlens, dev, T)
     shape = (H, d, fp8_vt_stride_packed(T, B)) if transpose else (T, H, d)
     # the columns past the last sequence's padding are not written: zero them
     out = (torch.zeros if transpose else torch.empty)(shape, dtype=torch.uint8, device=dev) if out is None else out
@@ -634,7 +657,7 @@ def fwd_fp8_packed(q8: torch.Tensor, k8: torch.Tensor, vt8: torch.Tensor, descal
     if q8.dim() != 3:
         raise ValueError("packed q8 must be [T, H, d]")
     T, H, d = (int(v) for v in q8.shape)
-    B = _packed_cu(cu_seqlens, dev)
+    B = _packed_cu(cu_seqlens, dev, T)
     if tuple(k8.shape) != (T, H, d) or tuple(vt8.shape) != (H, d, fp8_vt_stride_packed(T, B)):
         raise ValueError("k8 must be like q8 and vt8 [H, d, fp8_vt_stride_packed(T, B)]")
     for t, name in ((descale_q, "descale_q"), (descale_k, "descale_k"), (descale_v, "descale_v")):

@@ -106,7 +106,12 @@ enum fa_rescale_mode {
  *             finite and > 0.
  *   causal    0 or non-zero (lower-triangular mask).
  *   cu_seqlens NULL (dense) or a device int32 array of B+1 non-decreasing
- *             offsets with cu_seqlens[0] = 0 and cu_seqlens[B] = N.
+ *             offsets with cu_seqlens[0] = 0 and cu_seqlens[B] = N.  Its
+ *             contents are read on the device and not validated (no
+ *             synchronisation); every kernel clamps sequence b to tokens
+ *             [clamp(cu[b], 0, N), clamp(cu[b+1], that, N)), so malformed
+ *             offsets give wrong results, never accesses outside the
+ *             buffers.  This holds for every packed entry point.
  *   stream    HIP stream the kernel is queued on (NULL: default stream).
  * Returns FA_OK or an fa_status code.  Uses the library's default variant:
  * hardware exp2 and the strict conditional rescale (O and l are rescaled only
@@ -406,8 +411,10 @@ int fa_fp8_vt_stride(int N);
  * names variable-length sequences as a case of the tile scheduler): B
  * sequences in T tokens, cu_seqlens as fa_fwd's (device int32 [B + 1],
  * cu_seqlens[0] = 0, non-decreasing, cu_seqlens[B] = T; read on the device,
- * not validated).  Each sequence is its own attention problem with its own
- * per-head scales.
+ * not validated, clamped as fa_fwd's; a sequence whose padded keys would end
+ * past the V^T row, which only malformed offsets such as overlapping
+ * sequences produce, is skipped).  Each sequence is its own attention
+ * problem with its own per-head scales.
  *
  * fa_fp8_vt_stride_packed: row length (keys) of the packed transposed V
  * layout [H, d, Tp]: Tp = ceil(T / 64) * 64 + 64 B, which holds every

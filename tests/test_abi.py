@@ -440,3 +440,13 @@ def call_masked_p(lib, q=Q, k=K, v=V, o=O, lse=L, cu=CU8, B=2, H=2, T=100, d=128
 ])
 def test_masked_packed_invalid_arguments_are_rejected(lib, kw, code):
     assert call_masked_p(lib, **kw) == code
+
+
+def test_check_cu_seqlens():
+    """The host check of packed offsets (FA_CHECK_CU_SEQLENS=1 runs it before
+    every packed call)."""
+    import torch
+    fa.check_cu_seqlens(torch.tensor([0, 5, 5, 12], dtype=torch.int32), 12)
+    for bad, T in (([1, 5, 12], 12), ([0, 5, 12], 11), ([0, 7, 5, 12], 12), ([0, -1, 12], 12), ([0], 0)):
+        with pytest.raises(ValueError):
+            fa.check_cu_seqlens(torch.tensor(bad, dtype=torch.int32), T)
