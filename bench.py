@@ -372,6 +372,11 @@ def other_pass(torch, fa, which, workload, steps, warmup, settle_s=0.0):
         def launch():
             fa.fwd_splitkv(q, k, v, causal=r.causal, scale=ri["scale"], splits=S, out=o, lse=lse, o_part=op,
                            lse_part=lp)
+    elif which == "pingpong":
+        label += ", the two query tiles of a workgroup half a key tile apart"
+
+        def launch():
+            fa.fwd(q, k, v, causal=r.causal, scale=ri["scale"], out=o, lse=lse, pingpong=True)
     else:
         W = 1024
         slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / r.H) for h in range(r.H)], dtype=torch.float32,
@@ -450,10 +455,12 @@ def main() -> int:
     ap.add_argument("--extra", type=int, default=1, help="also time the other runs and variants")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "fp8", "split", "masked"), default="fwd",
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "fp8", "split", "masked", "pingpong"),
+                    default="fwd",
                     help="time only one other kernel family on --workload (for profiling): bwd = the "
                          "backward pass, fp8 = the FP8 forward, split = the split-KV forward and merge, "
-                         "masked = the 1024-key sliding window with ALiBi (fixed shape)")
+                         "masked = the 1024-key sliding window with ALiBi (fixed shape), pingpong = the "
+                         "two-query-tile ping-pong schedule of the forward (d = 128, dense)")
     ap.add_argument("--settle-s", type=float, default=0.5,
                     help="seconds of untimed launches before the warmup, so that the timed steps "
                          "run at the clock the GPU holds under this load (0: none)")
@@ -486,7 +493,7 @@ def main() -> int:
             "config": {"workload": f"{args.workload}: {res['shape']}"}, "roofline": res["roofline"],
             "kernel_fingerprint": kernel_fingerprint()}), flush=True)
         return 0
-    if args.which in ("fp8", "split", "masked"):
+    if args.which in ("fp8", "split", "masked", "pingpong"):
         res, f, ms_step, ms_kernel, label = other_pass(torch, fa, args.which, args.workload, args.steps,
                                                        args.warmup, args.settle_s)
         print(json.dumps({

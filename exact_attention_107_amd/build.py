@@ -5,7 +5,9 @@ with the C ABI unit into exact_attention_107_amd/libfa.so.
 """
 from __future__ import annotations
 
+import json
 import os
+import re
 import subprocess
 import sys
 import tempfile
@@ -58,24 +60,53 @@ def _clean(stderr: str) -> str:
                      if "packed-fp32-ops' is not a recognized feature" not in l)
 
 
+# Per-kernel register, scratch and LDS use reported by the compiler
+# (kernel-resource-usage remarks), written next to the library by build().
+RESOURCES_PATH = os.path.join(os.path.dirname(LIB_PATH), "libfa.resources.json")
+
+
+def _resources(stderr: str) -> dict:
+    """Kernel name -> resource fields from hipcc's kernel-resource-usage
+    remarks (demangled with c++filt when it is available)."""
+    rows, cur = {}, None
+    for line in stderr.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            cur = rows.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+([A-Za-z][A-Za-z \[\]/]*?): (\w+) \[", line)
+        if m and cur is not None:
+            cur[m.group(1).strip()] = int(m.group(2)) if m.group(2).isdigit() else m.group(2)
+    names = list(rows)
+    try:
+        out = subprocess.run(["c++filt"], input="\n".join(names), capture_output=True, text=True,
+                             check=True).stdout.splitlines()
+        if len(out) == len(names):
+            return {d: rows[n] for n, d in zip(names, out)}
+    except (OSError, subprocess.CalledProcessError):
+        pass
+    return rows
+
+
 def build(verbose: bool = False) -> str:
     with tempfile.TemporaryDirectory(prefix="fa_build_") as tmp:
         procs, objs = [], []
         for unit, extra in UNITS:
             obj = os.path.join(tmp, unit.replace(".hip", ".o"))
-            cmd = [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, unit), "-o", obj]
+            cmd = [HIPCC, *COMMON, *extra, "-Rpass-analysis=kernel-resource-usage", "-c",
+                   os.path.join(CSRC, unit), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((unit, subprocess.Popen(cmd, stdout=subprocess.PIPE,
                                                  stderr=subprocess.PIPE, text=True)))
             objs.append(obj)
-        failed = []
+        failed, resources = [], {}
         for unit, p in procs:
             _, err = p.communicate()
             if p.returncode != 0:
                 failed.append(f"{unit}:\n{_clean(err)}")
-            elif verbose and _clean(err).strip():
-                print(_clean(err), file=sys.stderr)
+            else:
+                resources.update({k: dict(v, unit=unit) for k, v in _resources(err).items()})
         if failed:
             raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
         out_tmp = LIB_PATH + ".tmp"
@@ -84,6 +115,8 @@ def build(verbose: bool = False) -> str:
         if res.returncode != 0:
             raise RuntimeError(f"link failed:\n{_clean(res.stderr)}")
         os.replace(out_tmp, LIB_PATH)
+    with open(RESOURCES_PATH, "w") as f:
+        json.dump(resources, f, indent=1, sort_keys=True)
     return LIB_PATH
 
 

@@ -468,10 +468,12 @@ fa_bwd_dkdv_kernel(BwdParams p) {
         if (qb + 1 < nqb) dma_block(qb + 1, PAR ? q_lds0 : q_lds1, PAR ? do_lds0 : do_lds1, PAR ? st_lds0 : st_lds1);
         const int q0 = qb * BQ;
         // causal: queries q0 .. q0+31 all precede this wave's keys -> nothing
-        // to add (for D = 256 the block runs anyway, fully masked: the first
-        // `wave` blocks of waves 1..3; branching round it makes the compiler
-        // spill the 256 accumulator registers)
-        if (!CAUSAL || D == 256 || q0 + BQ - 1 >= kw0) {
+        // to add.  Only D = 64 skips such a block; for D = 128 and 256 it runs
+        // fully masked (P = dS = 0 add exact zeros; the first `wave` blocks of
+        // waves 1..3, about 1 % of a long causal run's blocks): branching round
+        // it makes the compiler spill the accumulators (d = 128: 136 VGPRs,
+        // 3.7 times slower)
+        if (!CAUSAL || D != 64 || q0 + BQ - 1 >= kw0) {
             block(qcur, dcur, scur, q0, key_tail || q0 + BQ > n || (CAUSAL && q0 < kw0 + KW));
         }
         __builtin_amdgcn_s_waitcnt(0);

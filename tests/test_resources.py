@@ -1,0 +1,73 @@
+"""Register allocation of the built kernels (CPU): the compiler's
+kernel-resource-usage report that build() writes next to the library.
+
+A kernel that spills to scratch memory runs several times slower (a causal
+backward instance once did, 3.7 times, without any test noticing), so every
+default instance must use no scratch; the measurement-only counting
+instances, the masked instances (mask limits per lane and a bias) and the
+forward variants other than the default (polynomial or mixed exp2, the
+always and threshold rescale rules) may use a little."""
+import json
+import os
+
+import pytest
+
+from exact_attention_107_amd import build as fabuild
+
+# instances allowed a small amount of scratch (bytes per lane)
+SMALL_SCRATCH = 128
+
+
+def _report():
+    if not os.path.exists(fabuild.RESOURCES_PATH):
+        pytest.skip("no resource report: build the library with __graft_entry__.build()")
+    with open(fabuild.RESOURCES_PATH) as f:
+        return json.load(f)
+
+
+def _fwd_args(name: str):
+    """Template arguments of a forward instance: D, BC, NW, QB, CAUSAL,
+    VARLEN, EXPM, RSM, SPLIT, MODS, COUNT, PING."""
+    return name[name.index("<") + 1:name.index(">(")].split(", ")
+
+
+def _is_default_fwd(name: str) -> bool:
+    """fa_fwd's own instances: hardware exp2, strict rescale, no extras."""
+    a = _fwd_args(name)
+    return a[6] == "0" and a[7] == "1" and a[8:] == ["false"] * 4
+
+
+def _allowed(name: str) -> int:
+    if name.startswith("void fa_detail::fa_fwd_kernel<"):
+        a = _fwd_args(name)
+        if a[9] == "true" or a[10] == "true" or not (a[6] == "0" and a[7] == "1"):
+            return SMALL_SCRATCH
+    return 0
+
+
+def test_report_covers_every_unit():
+    rep = _report()
+    units = {v["unit"] for v in rep.values()}
+    assert {u for u, _ in fabuild.UNITS} - {"fa_api.hip"} <= units
+    kinds = ("fa_fwd_kernel<", "fa_bwd_dkdv_kernel<", "fa_bwd_dq_kernel<", "fa_fp8_fwd_kernel<", "merge")
+    for k in kinds:
+        assert any(k in n for n in rep), k
+
+
+def test_no_scratch_in_production_kernels():
+    rep = _report()
+    bad = {n: v.get("ScratchSize [bytes/lane]") for n, v in rep.items()
+           if int(v.get("ScratchSize [bytes/lane]", 0)) > _allowed(n)}
+    assert not bad, f"kernels using scratch memory: {bad}"
+
+
+def test_occupancy_of_the_default_forward():
+    """The d = 128 default forward keeps two waves per SIMD (eight-wave
+    workgroups), the d = 64 one three."""
+    rep = _report()
+    occ = {n: int(v.get("Occupancy [waves/SIMD]", 0)) for n, v in rep.items()
+           if n.startswith("void fa_detail::fa_fwd_kernel<") and _is_default_fwd(n)}
+    d128 = [o for n, o in occ.items() if n.startswith("void fa_detail::fa_fwd_kernel<128, 64, 8, 1,")]
+    d64 = [o for n, o in occ.items() if n.startswith("void fa_detail::fa_fwd_kernel<64, 64, 4, 1,")]
+    assert len(d128) == 4 and min(d128) >= 2      # causal x packed
+    assert len(d64) == 4 and min(d64) >= 3
