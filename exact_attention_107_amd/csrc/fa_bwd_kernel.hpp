@@ -635,15 +635,22 @@ fa_bwd_dq_kernel(BwdParams p) {
                 sf[2 * kb2 + t] = __builtin_bit_cast(bf16x8, su);
             }
         }
-        // dQ^T += K^T dS^T (K read transposed), k step t16 = 16 keys
-        static_for<0, NDB>([&](auto db_) {
-            constexpr int db = decltype(db_)::value;
-            static_for<0, 2 * NKB>([&](auto t_) {
-                constexpr int t16 = decltype(t_)::value;
-                bf16x8 ka = lds_tr<t16 * 16 * RB>(kb, ad.tr(db, 0), ad.tr(db, 1));
-                lgkm_wait<0>(ka);
-                dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, sf[t16], dqacc[db], 0, 0, 0);
-            });
+        // dQ^T += K^T dS^T (K read transposed): step m = (d block m / T16, k
+        // step m % T16 of 16 keys); the next step's fragment is read while
+        // this one multiplies (two reads in flight at the wait)
+        constexpr int T16 = 2 * NKB, MS = NDB * T16;
+        bf16x8 kt[2];
+        kt[0] = lds_tr<0>(kb, ad.tr(0, 0), ad.tr(0, 1));
+        static_for<0, MS>([&](auto m_) {
+            constexpr int m = decltype(m_)::value, db = m / T16, t16 = m % T16, cur = m & 1;
+            if constexpr (m + 1 < MS) {
+                constexpr int db1 = (m + 1) / T16, t1 = (m + 1) % T16;
+                kt[cur ^ 1] = lds_tr<t1 * 16 * RB>(kb, ad.tr(db1, 0), ad.tr(db1, 1));
+                lgkm_wait<2>(kt[cur]);
+            } else {
+                lgkm_wait<0>(kt[cur]);
+            }
+            dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[cur], sf[t16], dqacc[db], 0, 0, 0);
         });
     };
 
