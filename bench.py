@@ -254,7 +254,7 @@ PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS  # dense E4M3 MFMA rate is twice BF16's
 
 def fp8_setup(torch, fa, r, ri):
     """Device inputs of one FP8 run, quantised per (sequence, head); returns
-    (q, launch of the forward, quantisation of q into its codes)."""
+    (q, launch of the forward, quantisation of q into its codes, (o, lse))."""
     q, k, v = (to_dev(ri[x], torch) for x in ("q", "k", "v"))
     o = torch.empty_like(q)
     if ri["cu_seqlens"] is not None:
@@ -269,7 +269,7 @@ def fp8_setup(torch, fa, r, ri):
 
         def quant():
             fa.quantize_fp8_packed(q, cu, out=q8, descale=dq)
-        return q, launch, quant
+        return q, launch, quant, (o, lse)
     q8, dq = fa.quantize_fp8(q)
     k8, dk = fa.quantize_fp8(k)
     vt8, dv = fa.quantize_fp8(v, transpose=True)
@@ -280,7 +280,7 @@ def fp8_setup(torch, fa, r, ri):
 
     def quant():
         fa.quantize_fp8(q, out=q8, descale=dq)
-    return q, launch, quant
+    return q, launch, quant, (o, lse)
 
 
 def fp8_runs(torch, fa):
@@ -294,7 +294,7 @@ def fp8_runs(torch, fa):
         r = RUNS[name]
         log(f"[bench] fp8 run {name}")
         ri = make_inputs(r)
-        q, launch, quant = fp8_setup(torch, fa, r, ri)
+        q, launch, quant, _ = fp8_setup(torch, fa, r, ri)
         f = flops(ri["lengths"], r.H, r.d, r.causal)
 
         _, ms, _, _ = time_launches(launch, 30, 30, torch)
@@ -362,7 +362,7 @@ def other_pass(torch, fa, which, workload, steps, warmup, settle_s=0.0):
     label = f"{r.name}: B={r.B} H={r.H} N={r.N} d={r.d} causal={r.causal}"
     res = {}
     if which == "fp8":
-        _, launch, _ = fp8_setup(torch, fa, r, ri)
+        _, launch, _, _ = fp8_setup(torch, fa, r, ri)
     elif which == "split":
         S = fa.num_splits(r.B, r.H, r.N, r.d, r.causal, torch.cuda.get_device_properties(0).multi_processor_count)
         op = torch.empty((S, r.B, r.N, r.H, r.d), dtype=torch.float32, device="cuda")

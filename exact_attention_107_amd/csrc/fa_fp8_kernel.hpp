@@ -228,9 +228,16 @@ fa_fp8_fwd_kernel(Fp8Params p) {
         m_use8 = m_use - 8.0f;
         l_run *= alpha;
     };
-    // 2^8 P in E4M3, its sum, the regrouping into operand order, and
-    // O^T += V^T P^T
-    auto p_pv = [&](const f32x16 (&s)[2], const char *vtile) __attribute__((always_inline)) {
+    // O rescale of the strict rule: a wave-uniform branch at the top of a
+    // step, before the P V MFMAs accumulate onto O
+    auto o_rescale = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+    };
+    // 2^8 P in E4M3 and its sum, regrouped into operand order
+    auto p_exp = [&](const f32x16 (&s)[2], i32x8 &pb) __attribute__((always_inline)) {
         int pk[2][4];
         float rsum = 0.0f;
 #pragma unroll
@@ -247,19 +254,15 @@ fa_fp8_fwd_kernel(Fp8Params p) {
             }
         l_run += rsum;
         // lower half takes block 0's keys, upper half block 1's, in key order
-        i32x8 pb;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const auto sw = __builtin_amdgcn_permlane32_swap(pk[0][g], pk[1][g], false, false);
             pb[2 * g] = sw[0];
             pb[2 * g + 1] = sw[1];
         }
-        if (rescale_o) {
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-        }
+    };
+    // O^T += V^T P^T
+    auto pv_mfma = [&](const char *vtile, const i32x8 &pb) __attribute__((always_inline)) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
             oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(row32(vtile, db * 32 + c, 2 * hh, VRBc{}), pb,
@@ -268,9 +271,11 @@ fa_fp8_fwd_kernel(Fp8Params p) {
 
     // Pipeline: LDS holds K(j+1) and V(j) while K(j+2) and V(j+1) stream in
     // (into the buffers of K(j) and V(j-1), both consumed before the previous
-    // barrier).  Iteration j issues the S(j+1) MFMAs, then the weights of
-    // S(j) (VALU, independent of them) and the P V(j) MFMAs, then the row max
-    // of S(j+1).
+    // barrier).  A step j issues those loads, the S(j+1) MFMAs, the weights of
+    // S(j) (VALU, independent of them, in the same basic block so that the two
+    // interleave) and the P V(j) MFMAs, then the row max of S(j+1).  The
+    // steady-state steps carry no branch: the mask, the last tile and the
+    // tiles past a wave's causal horizon have steps of their own.
     f32x16 sa[2], sb[2];
     auto dma_k = [&](int j, char *kd) __attribute__((always_inline)) {
         const int kv0 = j * BC;
@@ -307,30 +312,76 @@ fa_fp8_fwd_kernel(Fp8Params p) {
     }
     __syncthreads();  // K(0)'s buffer takes K(2) next
 
-    auto step = [&](auto par_, f32x16 (&cur)[2], f32x16 (&nxt)[2], int j) __attribute__((always_inline)) {
-        constexpr int PAR = decltype(par_)::value;  // j & 1
+    auto issue_loads = [&](int j, char *kbuf_j, char *vbuf_n) __attribute__((always_inline)) {
+        if (j + 2 < nkv) dma_k(j + 2, kbuf_j);
+        if (j + 1 < nkv) dma_v(j + 1, vbuf_n);
+    };
+    auto end_iteration = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    };
+    // a step whose tiles j and j + 1 this wave both computes; PAR = j & 1
+    // selects the LDS buffers, MASK whether S(j+1) needs the tail or causal mask
+    auto full_step = [&](auto par_, auto mask_, f32x16 (&cur)[2], f32x16 (&nxt)[2], int j)
+                         __attribute__((always_inline)) {
+        constexpr int PAR = decltype(par_)::value;
         char *kbuf_j = PAR ? k_lds1 : k_lds0;       // held K(j), takes K(j+2)
         char *kbuf_n = PAR ? k_lds0 : k_lds1;       // holds K(j+1)
         char *vbuf_j = PAR ? v_lds1 : v_lds0;       // holds V(j)
         char *vbuf_n = PAR ? v_lds0 : v_lds1;       // held V(j-1), takes V(j+1)
-        if (j + 2 < nkv) dma_k(j + 2, kbuf_j);
-        if (j + 1 < nkv) dma_v(j + 1, vbuf_n);
-        const bool has_next = j + 1 < nkv_w;
-        if (has_next) s_mfma(nxt, kbuf_n);
-        if (j < nkv_w) p_pv(cur, vbuf_j);
-        if (has_next) {
-            if (need_mask(j + 1)) s_mask(nxt, j + 1);
-            s_update(nxt);
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        issue_loads(j, kbuf_j, vbuf_n);
+        if (rescale_o) o_rescale();
+        __builtin_amdgcn_sched_barrier(0);
+        s_mfma(nxt, kbuf_n);
+        i32x8 pb;
+        p_exp(cur, pb);
+        pv_mfma(vbuf_j, pb);
+        if constexpr (decltype(mask_)::value) s_mask(nxt, j + 1);
+        s_update(nxt);
+        __builtin_amdgcn_sched_barrier(0);
+        end_iteration();
     };
+    // the wave's last tile: no next S
+    auto drain_step = [&](auto par_, const f32x16 (&cur)[2], int j) __attribute__((always_inline)) {
+        constexpr int PAR = decltype(par_)::value;
+        issue_loads(j, PAR ? k_lds1 : k_lds0, PAR ? v_lds0 : v_lds1);
+        if (rescale_o) o_rescale();
+        i32x8 pb;
+        p_exp(cur, pb);
+        pv_mfma(PAR ? v_lds1 : v_lds0, pb);
+        end_iteration();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using NoMask = std::integral_constant<bool, false>;
+    using Mask = std::integral_constant<bool, true>;
+    // first tile that needs a mask (tail: n / BC; causal: (wrow0 + 1) / BC)
+    const int jm = CAUSAL ? min(n / BC, (wrow0 + 1) / BC) : n / BC;
+    const int lim = min(nkv_w, jm);
     int j = 0;
-    for (; j + 1 < nkv; j += 2) {
-        step(std::integral_constant<int, 0>{}, sa, sb, j);
-        step(std::integral_constant<int, 1>{}, sb, sa, j + 1);
+    for (; j + 2 < lim; j += 2) {
+        full_step(I0{}, NoMask{}, sa, sb, j);
+        full_step(I1{}, NoMask{}, sb, sa, j + 1);
     }
-    if (j < nkv) step(std::integral_constant<int, 0>{}, sa, sb, j);
+    for (; j + 2 < nkv_w; j += 2) {
+        full_step(I0{}, Mask{}, sa, sb, j);
+        full_step(I1{}, Mask{}, sb, sa, j + 1);
+    }
+    if (j + 1 < nkv_w) {
+        full_step(I0{}, Mask{}, sa, sb, j);
+        ++j;
+    }
+    if (j < nkv_w) {
+        if (j & 1) drain_step(I1{}, sb, j);
+        else drain_step(I0{}, sa, j);
+        ++j;
+    }
+    // tiles past this wave's causal horizon: keep loading for the other waves
+    for (; j < nkv; ++j) {
+        if (j & 1) issue_loads(j, k_lds1, v_lds0);
+        else issue_loads(j, k_lds0, v_lds1);
+        end_iteration();
+    }
 
     // epilogue: O = O^T dv / l (l sums 2^8 P like O), LSE = (m + log2 l - 8) ln 2
     const float l = xhalf_sum(l_run);
