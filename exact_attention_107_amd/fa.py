@@ -275,7 +275,7 @@ def fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bo
                 out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
                 o_part: torch.Tensor | None = None, lse_part: torch.Tensor | None = None,
                 stream: torch.cuda.Stream | None = None):
-    """Split-KV forward (``fa_fwd_splitkv``), dense ``[B, N, H, d]`` only.
+    """Split-KV forward (``fa_fwd_splitkv``), dense ``[B, N, H, d]`` (packed: ``fwd_splitkv_packed``).
 
     ``splits`` defaults to the library's suggestion for this device.  The fp32
     workspaces ``o_part [S, B, N, H, d]`` and ``lse_part [S, B, H, N]`` are
