@@ -45,6 +45,14 @@ def workload_label(run, inp) -> str:
     return f"{run.name}: {shape} causal={inp['causal']} {dist}, V~N(0,1)"
 
 
+def fwd_rows(fa, torch, inp) -> int:
+    """Rows per workgroup that fa_fwd picks for the input's shape on this GPU."""
+    cu = inp.get("cu_seqlens")
+    n = int(cu[-1]) if cu is not None else inp["N"]
+    return fa.fwd_tile_rows(inp["B"], inp["H"], n, inp["d"], inp["causal"], cu is not None,
+                            torch.cuda.get_device_properties(0).multi_processor_count)
+
+
 def kernel_fingerprint() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
@@ -542,7 +550,7 @@ def main() -> int:
         "config": {
             "workload": workload_label(run, inp),
             "B": inp["B"], "H": inp["H"], "N": inp["N"], "d": inp["d"], "causal": inp["causal"],
-            "flops_per_step": f, "tile_rows": fa.tile_rows(inp["d"]), "tile_keys": fa.tile_keys(inp["d"]),
+            "flops_per_step": f, "tile_rows": fwd_rows(fa, torch, inp), "tile_keys": fa.tile_keys(inp["d"]),
         },
         "clock_settle": {"seconds": args.settle_s, "launches": settle_launches,
                          "note": "untimed launches before the warmup steps"},

@@ -6,6 +6,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "fa.h"
@@ -67,6 +68,42 @@ int scratch_for_current_device(void **out) {
     return FA_OK;
 }
 
+// Compute units of the current GPU, asked once per device and kept (0 when
+// HIP cannot say).  Only the choice of workgroup shape depends on it.
+std::atomic<int> g_cus[kMaxDevices];
+
+int cus_of_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int n = g_cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 0)
+            n = 0;
+        g_cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Rows per workgroup of the default forward.  At d = 128 an eight-wave
+// workgroup (256 rows) is the fastest shape once the grid covers the GPU
+// several times over; four-wave workgroups (128 rows, two resident per
+// compute unit) win when the eight-wave grid would leave compute units idle
+// or end in a short last round: a non-causal grid of at most half a workgroup
+// per compute unit, or between one and two with the second round at most
+// half full; a causal grid of at most one per compute unit, whose tiles of
+// unequal length the finer grid balances.
+int default_rows(int B, int H, int N, int d, bool causal, bool packed, int num_cus) {
+    if (d != 128) return tile_rows_for(d);
+    const long long cus = num_cus > 0 ? num_cus : 256;
+    const long long items = (packed ? 1LL : static_cast<long long>(B)) * H * ((N + 255LL) / 256);
+    bool four;
+    if (causal)
+        four = items <= cus;
+    else
+        four = 2 * items <= cus || (items > cus && items < 2 * cus && 2 * (items - cus) <= cus);
+    return four ? 128 : 256;
+}
+
 }  // namespace
 
 extern "C" {
@@ -92,12 +129,19 @@ int fa_tile_rows(int d) { return tile_rows_for(d); }
 
 int fa_tile_keys(int d) { return (d == 64 || d == 128 || d == 256) ? kTileKeys : 0; }
 
+int fa_fwd_tile_rows(int B, int H, int N, int d, int causal, int packed, int num_cus) {
+    if (tile_rows_for(d) == 0) return 0;
+    if (B < 1 || H < 1 || N < 1) return tile_rows_for(d);
+    return default_rows(B, H, N, d, causal != 0, packed != 0, num_cus);
+}
+
 // Validation and launch of the forward; `counts` selects the counting
-// instance (d = 128, hardware exp2) and receives its statistics.
+// instance (d = 128, hardware exp2) and receives its statistics; `adapt`
+// lets the shape of the grid choose the workgroup shape (fa_fwd).
 static int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
                     int N, int d, float scale, int causal, const int32_t *cu_seqlens,
                     hipStream_t stream, int exp_mode, int rescale_mode, unsigned long long *counts,
-                    bool ping = false) {
+                    bool ping = false, bool adapt = false) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULLPTR;
     if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
     if (d != 64 && d != 128 && d != 256) return FA_ERR_HEAD_DIM;
@@ -131,7 +175,13 @@ static int fwd_impl(const void *q, const void *k, const void *v, void *o, float 
     prm.H = H;
     prm.N = N;
     prm.cs = scale * kLog2e;
-    const int rows = tile_rows_for(d);
+    // fa_fwd picks its workgroup shape for the grid; fa_fwd_variant (the
+    // default instance included), the counting and the ping-pong instances
+    // keep theirs
+    const bool plain = adapt && !counts && !ping && exp_mode == FA_EXP_HW && rescale_mode == FA_RESCALE_STRICT;
+    const int rows = plain ? default_rows(B, H, N, d, causal != 0, varlen, cus_of_current_device())
+                           : tile_rows_for(d);
+    const bool quad = d == 128 && rows == 128;
     const long long n_qt = (static_cast<long long>(N) + rows - 1) / rows;
     prm.n_qt = static_cast<int>(n_qt);
     long long grid;
@@ -144,10 +194,12 @@ static int fwd_impl(const void *q, const void *k, const void *v, void *o, float 
 
     prm.counts = counts;
     KernelFn fn = counts ? select_count_d128(causal != 0, varlen, rescale_mode)
-                         : (ping ? select_ping_d128(causal != 0, varlen)
-                                 : pick(d, causal != 0, varlen, exp_mode, rescale_mode));
+                  : ping ? select_ping_d128(causal != 0, varlen)
+                  : quad ? select_quad_d128(causal != 0, varlen)
+                         : pick(d, causal != 0, varlen, exp_mode, rescale_mode);
+    const int threads = (quad ? 4 : waves_for(d)) * 64;
     (void)hipGetLastError();  // clear a stale error so the check below is ours
-    hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(grid)), dim3(waves_for(d) * 64), 0, stream, prm);
+    hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(grid)), dim3(threads), 0, stream, prm);
     if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
     return FA_OK;
 }
@@ -653,8 +705,8 @@ int fa_fwd_variant(const void *q, const void *k, const void *v, void *o, float *
 
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
            int d, float scale, int causal, const int32_t *cu_seqlens, hipStream_t stream) {
-    return fa_fwd_variant(q, k, v, o, lse, B, H, N, d, scale, causal, cu_seqlens, stream,
-                          FA_EXP_HW, FA_RESCALE_STRICT);
+    return fwd_impl(q, k, v, o, lse, B, H, N, d, scale, causal, cu_seqlens, stream, FA_EXP_HW, FA_RESCALE_STRICT,
+                    nullptr, false, true);
 }
 
 int fa_fwd_pingpong(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,

@@ -82,6 +82,9 @@ KernelFn select_count_d128(bool causal, bool varlen, int rescale_mode);
 // The default forward (hardware exp2, strict rescale) with the two halves of
 // the eight-wave workgroup run half a key tile apart (head dimension 128).
 KernelFn select_ping_d128(bool causal, bool varlen);
+// The default forward at head dimension 128 in four-wave (128-row)
+// workgroups, for grids that would leave compute units idle.
+KernelFn select_quad_d128(bool causal, bool varlen);
 // Window-mask / linear-bias instance (dense or packed layout).
 KernelFn select_mods_d64(bool varlen);
 KernelFn select_mods_d128(bool varlen);

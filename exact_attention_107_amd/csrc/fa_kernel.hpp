@@ -1183,6 +1183,19 @@ KernelFn select_mods(bool varlen) {
     return fa_fwd_kernel<D, BC, NW, QB, false, false, FA_EXP_HW, FA_RESCALE_THRESHOLD, false, true>;
 }
 
+// The default forward (hardware exp2, strict rescale) in four-wave
+// workgroups of 128 rows, for shapes whose eight-wave grid would leave
+// compute units idle; each wave's rows see the same tiles in the same order,
+// so its results are bitwise those of the eight-wave instance.
+template <int D>
+KernelFn select_quad(bool causal, bool varlen) {
+    constexpr int BC = kTileKeys;
+    if (causal) return varlen ? fa_fwd_kernel<D, BC, 4, 1, true, true, FA_EXP_HW, FA_RESCALE_STRICT>
+                              : fa_fwd_kernel<D, BC, 4, 1, true, false, FA_EXP_HW, FA_RESCALE_STRICT>;
+    return varlen ? fa_fwd_kernel<D, BC, 4, 1, false, true, FA_EXP_HW, FA_RESCALE_STRICT>
+                  : fa_fwd_kernel<D, BC, 4, 1, false, false, FA_EXP_HW, FA_RESCALE_STRICT>;
+}
+
 template <int D>
 KernelFn select_split(bool causal, bool varlen) {
     constexpr int BC = kTileKeys, NW = Geometry<D>::kWaves, QB = Geometry<D>::kBlocks;

@@ -17,4 +17,6 @@ KernelFn select_count_d128(bool causal, bool varlen, int rescale_mode) {
 
 KernelFn select_ping_d128(bool causal, bool varlen) { return select_ping<128>(causal, varlen); }
 
+KernelFn select_quad_d128(bool causal, bool varlen) { return select_quad<128>(causal, varlen); }
+
 }  // namespace fa_detail

@@ -24,7 +24,7 @@ EXPORTS = ("fa_fwd", "fa_fwd_variant", "fa_strerror", "fa_tile_rows", "fa_tile_k
            "fa_bwd_workspace_floats", "fa_fwd_fp8", "fa_quantize_fp8", "fa_fp8_vt_stride",
            "fa_fwd_masked", "fa_fwd_rescale_counts", "fa_fwd_splitkv_static", "fa_fwd_pingpong",
            "fa_fp8_vt_stride_packed", "fa_quantize_fp8_packed", "fa_fwd_fp8_packed", "fa_fwd_splitkv_packed",
-           "fa_fwd_masked_packed")
+           "fa_fwd_masked_packed", "fa_fwd_tile_rows")
 FA_ERR_SCRATCH = 10
 STATIC_SCRATCH_BYTES = 64 << 20   # FA_STATIC_SCRATCH_BYTES of include/fa.h
 
@@ -75,6 +75,8 @@ def load(path: str | None = None):
     lib.fa_tile_rows.restype = i32
     lib.fa_tile_keys.argtypes = [i32]
     lib.fa_tile_keys.restype = i32
+    lib.fa_fwd_tile_rows.argtypes = [i32] * 7
+    lib.fa_fwd_tile_rows.restype = i32
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_float, i32,
                                    i32, vp, vp, vp]
     lib.fa_fwd_splitkv.restype = i32
@@ -247,6 +249,13 @@ def tile_rows(d: int) -> int:
 
 def tile_keys(d: int) -> int:
     return int(load().fa_tile_keys(int(d)))
+
+
+def fwd_tile_rows(B: int, H: int, N: int, d: int, causal: bool = False, packed: bool = False,
+                  num_cus: int = 0) -> int:
+    """Rows per workgroup tile fa_fwd picks for a shape (packed: B sequences, N = T)."""
+    return int(load().fa_fwd_tile_rows(int(B), int(H), int(N), int(d), int(bool(causal)),
+                                       int(bool(packed)), int(num_cus)))
 
 
 def split_range(N: int, d: int, causal: bool, num_splits: int, s: int, row: int) -> tuple[int, int]:

@@ -119,6 +119,8 @@ enum fa_rescale_mode {
  * in bf16).  The threshold rule is faster on unit-variance inputs but lets a
  * dominant weight reach 2^8, which bf16 cannot hold exactly, so its instances
  * divide O by the sum of the bf16 weights at some cost (see fa_fwd_variant).
+ * The workgroup shape follows the size of the grid (fa_fwd_tile_rows); the
+ * results do not.
  */
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
            int B, int H, int N, int d, float scale, int causal,
@@ -128,6 +130,8 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
  * fa_fwd_variant: fa_fwd with an explicit exp evaluation (fa_exp_mode) and
  * rescale policy (fa_rescale_mode).  Every variant computes the same O and
  * LSE up to rounding, within the forward's tolerances; they differ in speed.
+ * Its workgroups always have fa_tile_rows(d) rows, so (FA_EXP_HW,
+ * FA_RESCALE_STRICT) is fa_fwd with the tile it uses on large grids.
  * Threshold instances divide O by the sum of the bf16-rounded weights that
  * the P V product uses (its reference max may trail a row's maximum by up to
  * 8, so a dominant weight is not exact in bf16); the LSE always uses the fp32
@@ -461,11 +465,28 @@ int fa_fwd_fp8_packed(const void *q8, const void *k8, const void *vt8,
 /* Static, NUL-terminated description of an fa_status code. */
 const char *fa_strerror(int code);
 
-/* Rows per workgroup tile and keys per K/V tile of the kernel that fa_fwd
- * would launch for head dimension d (0 for an unsupported d).  Informational;
- * used by benchmarks to report launch geometry. */
+/* Rows per workgroup tile and keys per K/V tile at head dimension d (0 for
+ * an unsupported d): the query tile of the split-KV, masked, counting,
+ * ping-pong and fa_fwd_variant instances, and of fa_fwd on grids that fill
+ * the GPU (fa_fwd_tile_rows gives fa_fwd's choice for a shape).
+ * Informational; no result depends on it. */
 int fa_tile_rows(int d);
 int fa_tile_keys(int d);
+
+/* Rows per workgroup tile that fa_fwd (hardware exp2, strict rescale) uses
+ * for a shape on a GPU with num_cus compute units (<= 0: 256, the MI355X);
+ * fa_fwd itself asks HIP for the current device's count once per device.
+ * B, N: batch and sequence length (packed: the sequence count and T).  At
+ * d = 128 the grid of 256-row eight-wave workgroups is replaced by 128-row
+ * four-wave ones when the former would leave compute units idle: non-causal
+ * with ceil(N / 256) * B * H (packed: * H alone) at most num_cus / 2, or
+ * between num_cus and 2 num_cus with the excess at most num_cus / 2; causal
+ * with it at most num_cus.  Each query row sees the same key tiles in the
+ * same order either way, so O and LSE are bitwise the same (finite inputs).
+ * Other d: their
+ * fixed tile.  0 for an unsupported d; fa_tile_rows(d) for B, H or N < 1.
+ * Informational, like fa_tile_rows. */
+int fa_fwd_tile_rows(int B, int H, int N, int d, int causal, int packed, int num_cus);
 
 #ifdef __cplusplus
 }

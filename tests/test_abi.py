@@ -67,6 +67,44 @@ def test_tile_geometry(lib):
     assert fa.tile_rows(96) == 0 and fa.tile_keys(32) == 0
 
 
+def test_fwd_tile_rows_rule(lib):
+    """fa_fwd's workgroup shape: 128-row four-wave tiles at d = 128 when the
+    256-row grid leaves compute units idle, as include/fa.h states it."""
+    ftr = fa.fwd_tile_rows
+    # other head dimensions keep their tile; bad d gives 0
+    for d in (64, 256):
+        for H in (1, 64):
+            assert ftr(1, H, 8192, d) == fa.tile_rows(d)
+    assert ftr(1, 4, 8192, 96) == 0
+    assert ftr(0, 4, 8192, 128) == fa.tile_rows(128) == 256
+    # non-causal, 256 CUs: items = B * H * ceil(N / 256)
+    assert ftr(1, 4, 8192, 128) == 128              # 128 items: half the CUs
+    assert ftr(1, 6, 8192, 128) == 256              # 192
+    assert ftr(1, 8, 8192, 128) == 256              # 256: one full round
+    assert ftr(1, 12, 8192, 128) == 128             # 384: second round half full
+    assert ftr(1, 13, 8192, 128) == 256             # 416: more than half
+    assert ftr(1, 8, 8193, 128) == 128              # 264 (ragged tail tile)
+    assert ftr(2, 16, 8192, 128) == 256             # 1024
+    assert ftr(1, 1, 1, 128) == 128
+    # causal: at most one item per CU
+    assert ftr(1, 8, 8192, 128, causal=True) == 128   # 256
+    assert ftr(1, 8, 16384, 128, causal=True) == 256  # 512
+    assert ftr(1, 12, 8192, 128, causal=True) == 256  # 384
+    # packed: B does not multiply (the sequences share the token axis)
+    assert ftr(8, 4, 8192, 128, packed=True) == 128
+    assert ftr(8, 4, 8192, 128) == 256
+    # the CU count scales the thresholds; <= 0 means 256
+    assert ftr(1, 4, 8192, 128, num_cus=128) == 256
+    assert ftr(1, 2, 8192, 128, num_cus=128) == 128
+    assert ftr(1, 4, 8192, 128, num_cus=-1) == 128
+    # exhaustive against the stated rule on a grid of shapes
+    for cus in (80, 256, 304):
+        for items in range(1, 3 * cus):
+            nc = 2 * items <= cus or (cus < items < 2 * cus and 2 * (items - cus) <= cus)
+            assert ftr(1, items, 256, 128, num_cus=cus) == (128 if nc else 256), (cus, items)
+            assert ftr(1, items, 200, 128, causal=True, num_cus=cus) == (128 if items <= cus else 256)
+
+
 # Fake but plausible device addresses: validation rejects before using them.
 Q, K, V, O, L = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
 

@@ -12,7 +12,7 @@ import torch
 
 from exact_attention_107_amd import fa
 from exact_attention_107_amd.workloads import RUNS, Run, make_inputs
-from gpu_helpers import assert_within, every_row_parity, from_dev, full_parity, run_gpu, to_dev
+from gpu_helpers import assert_within, every_row_parity, from_dev, full_parity, run_gpu, sampled_parity, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -217,3 +217,56 @@ def test_pingpong_ragged_and_edge(causal):
         assert_within(m, f"pingpong N={N} causal={causal}")
         o0, l0 = run_gpu(inp)
         assert torch.equal(o.view(torch.int16), o0.view(torch.int16)) and torch.equal(lse, l0)
+
+
+def _cus():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def _fixed_tile(inp):
+    """fa_fwd_variant with fa_fwd's own exp and rescale: always the
+    fa_tile_rows(d) workgroup."""
+    return run_gpu(inp, exp_mode=fa.EXP_HW, rescale_mode=fa.RESCALE_STRICT)
+
+
+def _rows_chosen(inp):
+    packed = inp.get("cu_seqlens") is not None
+    B = len(inp["lengths"])
+    N = int(inp["cu_seqlens"][-1]) if packed else int(inp["q"].shape[1])
+    return fa.fwd_tile_rows(B, inp["H"], N, inp["d"], inp["causal"], packed, _cus())
+
+
+@pytest.mark.parametrize("name", ["few_heads", "few_heads_causal"])
+def test_four_wave_tiles_full_size(name):
+    """The few-head runs, whose 256-row grid leaves compute units idle, take
+    the 128-row four-wave workgroups: sampled rows against the oracle, and
+    every element bitwise the 256-row instance's."""
+    inp = make_inputs(RUNS[name])
+    assert _rows_chosen(inp) == 128
+    o, lse = run_gpu(inp)
+    m = sampled_parity(inp, o, lse, count=512, seed=11)
+    print(name, m)
+    assert_within(m, name)
+    o8, l8 = _fixed_tile(inp)
+    assert torch.equal(o.view(torch.int16), o8.view(torch.int16)) and torch.equal(lse, l8)
+
+
+@pytest.mark.parametrize("name", ["mid", "wide"])
+def test_full_grids_keep_eight_waves(name):
+    inp = make_inputs(RUNS[name])
+    assert _rows_chosen(inp) == fa.tile_rows(128) == 256
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_four_wave_tiles_edges_and_packed(causal):
+    """Small shapes (four-wave tiles): every element against the oracle and
+    bitwise the 256-row instance; ragged lengths, single rows, packed."""
+    cases = [_small(128, causal, N=N, B=2, H=3, seed=900 + N) for N in (1, 2, 65, 127, 129, 255, 257, 1000)]
+    r = Run("packed", 5, 4, 0, 128, causal, 931)
+    cases.append(make_inputs(r, lengths=[1, 130, 0, 257, 700]))
+    for inp in cases:
+        assert _rows_chosen(inp) == 128
+        m, (o, lse) = full_parity(inp)
+        assert_within(m, f"four-wave lengths={list(inp['lengths'])} causal={causal}")
+        o8, l8 = _fixed_tile(inp)
+        assert torch.equal(o.view(torch.int16), o8.view(torch.int16)) and torch.equal(lse, l8)

@@ -63,11 +63,14 @@ def test_no_scratch_in_production_kernels():
 
 def test_occupancy_of_the_default_forward():
     """The d = 128 default forward keeps two waves per SIMD (eight-wave
-    workgroups), the d = 64 one three."""
+    workgroups, or two four-wave ones), the d = 64 one three."""
     rep = _report()
     occ = {n: int(v.get("Occupancy [waves/SIMD]", 0)) for n, v in rep.items()
            if n.startswith("void fa_detail::fa_fwd_kernel<") and _is_default_fwd(n)}
     d128 = [o for n, o in occ.items() if n.startswith("void fa_detail::fa_fwd_kernel<128, 64, 8, 1,")]
     d64 = [o for n, o in occ.items() if n.startswith("void fa_detail::fa_fwd_kernel<64, 64, 4, 1,")]
     assert len(d128) == 4 and min(d128) >= 2      # causal x packed
+    # the four-wave d = 128 tiles for small grids: two workgroups per CU
+    quad = [o for n, o in occ.items() if n.startswith("void fa_detail::fa_fwd_kernel<128, 64, 4, 1,")]
+    assert len(quad) == 4 and min(quad) >= 2
     assert len(d64) == 4 and min(d64) >= 3
