@@ -572,7 +572,8 @@ def main() -> int:
 
     if args.extra:
         runs = {}
-        for name in ("mid", "mid_causal", "long_causal", "varlen_causal", "wide_d64", "wide_d256"):
+        for name in ("mid", "mid_causal", "long_causal", "varlen_causal", "wide_d64", "wide_d256", "few_heads",
+                     "few_heads_causal"):
             r = RUNS[name]
             log(f"[bench] run {name}")
             ri = make_inputs(r)
@@ -588,7 +589,8 @@ def main() -> int:
 
             _, kms, _, _ = time_launches(rlaunch, 50, 50, torch)  # clocks settle as for the headline
             runs[name] = {"ms": round(kms, 4), "tflops": round(rf / (kms * 1e-3) / 1e12, 1),
-                          "pct_of_peak": round(100 * rf / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 1)}
+                          "pct_of_peak": round(100 * rf / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 1),
+                          "tile_rows": fwd_rows(fa, torch, ri)}
             del rq, rk, rv, ro, rl
         out["runs"] = runs
         variants = {}
