@@ -154,3 +154,21 @@ def test_sweep_backward(case):
         rel_max = float(diff.max()) / float(np.abs(ref).max())
         assert rel_rms <= GRAD_TOL_RMS and rel_max <= GRAD_TOL_MAX, \
             f"{label} {name}: rel_rms {rel_rms:.3e} rel_max {rel_max:.3e}"
+
+
+@pytest.mark.parametrize("case", range(CASES // 2))
+def test_sweep_fp8(case):
+    """fa_fwd_fp8 on dense draws: every element within the E4M3 error bound
+    of the FP8 tests (quantisation as the oracle defines it)."""
+    from test_fp8_gpu import _all_rows, _check_rows, _quantized, _run_fp8
+    rng = np.random.Generator(np.random.PCG64(5000 + case))
+    d = int(rng.choice([64, 128, 256]))
+    B, H, N = int(rng.integers(1, 4)), int(rng.integers(1, 6)), int(rng.integers(1, MAX_N))
+    causal = bool(rng.integers(2))
+    sigma = float(rng.choice([1.0, 3.0]))
+    inp = make_inputs(Run(f"sweep8_{case}", B, H, N, d, causal, 5000 + case, sigma_qk=sigma))
+    label = f"fp8 seed={5000 + case} d={d} B={B} H={H} N={N} causal={causal} sigma={sigma}"
+    print(label, flush=True)
+    qz = _quantized(inp)
+    o, lse = _run_fp8(*qz, inp["scale"], causal)
+    _check_rows(inp, causal, *qz, o, lse, _all_rows(B, H, N), label)
