@@ -270,3 +270,25 @@ def test_four_wave_tiles_edges_and_packed(causal):
         assert_within(m, f"four-wave lengths={list(inp['lengths'])} causal={causal}")
         o8, l8 = _fixed_tile(inp)
         assert torch.equal(o.view(torch.int16), o8.view(torch.int16)) and torch.equal(lse, l8)
+
+
+# (B, H, N, causal) at the edges of the rule: 256-row items = C/2, C, 1.5 C and
+# 2 C (+1) on a 256-CU MI355X
+BOUNDARY_SHAPES = [(1, 128, 256, False), (1, 129, 256, False), (1, 256, 256, False), (1, 257, 256, False),
+                   (1, 384, 256, False), (1, 385, 200, False), (2, 128, 512, False), (1, 512, 129, False),
+                   (1, 256, 256, True), (1, 257, 256, True), (2, 64, 300, True)]
+
+
+@pytest.mark.parametrize("shape", BOUNDARY_SHAPES, ids=lambda s: "B{}_H{}_N{}_{}".format(*s))
+def test_four_wave_rule_boundaries(shape):
+    """Shapes on either side of each threshold of the workgroup-shape rule:
+    sampled rows against the oracle and every element bitwise the 256-row
+    instance, whichever shape fa_fwd picks."""
+    B, H, N, causal = shape
+    inp = _small(128, causal, N=N, B=B, H=H, seed=1200 + H)
+    rows = _rows_chosen(inp)
+    o, lse = run_gpu(inp)
+    m = sampled_parity(inp, o, lse, count=256, seed=H)
+    assert_within(m, f"{shape} rows={rows}")
+    o8, l8 = _fixed_tile(inp)
+    assert torch.equal(o.view(torch.int16), o8.view(torch.int16)) and torch.equal(lse, l8), f"{shape} rows={rows}"
