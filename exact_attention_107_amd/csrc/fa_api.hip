@@ -89,18 +89,20 @@ int cus_of_current_device() {
 // several times over; four-wave workgroups (128 rows, two resident per
 // compute unit) win when the eight-wave grid would leave compute units idle
 // or end in a short last round: a non-causal grid of at most half a workgroup
-// per compute unit, or between one and two with the second round at most
-// half full; a causal grid of at most one per compute unit, whose tiles of
-// unequal length the finer grid balances.
+// per compute unit, or of one to three rounds whose last round is at most
+// half full; a causal grid of at most one and a half per compute unit, whose
+// tiles of unequal length the finer grid balances.
 int default_rows(int B, int H, int N, int d, bool causal, bool packed, int num_cus) {
     if (d != 128) return tile_rows_for(d);
     const long long cus = num_cus > 0 ? num_cus : 256;
     const long long items = (packed ? 1LL : static_cast<long long>(B)) * H * ((N + 255LL) / 256);
     bool four;
-    if (causal)
-        four = items <= cus;
-    else
-        four = 2 * items <= cus || (items > cus && items < 2 * cus && 2 * (items - cus) <= cus);
+    if (causal) {
+        four = 2 * items <= 3 * cus;
+    } else {
+        const long long last = items % cus;  // workgroups of the last round
+        four = 2 * items <= cus || (items > cus && items < 3 * cus && last > 0 && 2 * last <= cus);
+    }
     return four ? 128 : 256;
 }
 

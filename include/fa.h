@@ -478,14 +478,14 @@ int fa_tile_keys(int d);
  * fa_fwd itself asks HIP for the current device's count once per device.
  * B, N: batch and sequence length (packed: the sequence count and T).  At
  * d = 128 the grid of 256-row eight-wave workgroups is replaced by 128-row
- * four-wave ones when the former would leave compute units idle: non-causal
- * with ceil(N / 256) * B * H (packed: * H alone) at most num_cus / 2, or
- * between num_cus and 2 num_cus with the excess at most num_cus / 2; causal
- * with it at most num_cus.  Each query row sees the same key tiles in the
- * same order either way, so O and LSE are bitwise the same (finite inputs).
- * Other d: their
- * fixed tile.  0 for an unsupported d; fa_tile_rows(d) for B, H or N < 1.
- * Informational, like fa_tile_rows. */
+ * four-wave ones when the former would leave compute units idle: with
+ * items = ceil(N / 256) * B * H (packed: * H alone), non-causal when items is
+ * at most num_cus / 2, or strictly between num_cus and 3 num_cus with
+ * items mod num_cus in 1 .. num_cus / 2 (a last round at most half full);
+ * causal when items is at most 1.5 num_cus.  Each query row sees the same key
+ * tiles in the same order either way, so O and LSE are bitwise the same
+ * (finite inputs).  Other d: their fixed tile.  0 for an unsupported d;
+ * fa_tile_rows(d) for B, H or N < 1.  Informational, like fa_tile_rows. */
 int fa_fwd_tile_rows(int B, int H, int N, int d, int causal, int packed, int num_cus);
 
 #ifdef __cplusplus

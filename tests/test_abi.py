@@ -84,12 +84,18 @@ def test_fwd_tile_rows_rule(lib):
     assert ftr(1, 12, 8192, 128) == 128             # 384: second round half full
     assert ftr(1, 13, 8192, 128) == 256             # 416: more than half
     assert ftr(1, 8, 8193, 128) == 128              # 264 (ragged tail tile)
+    assert ftr(1, 16, 8192, 128) == 256             # 512: two full rounds
+    assert ftr(1, 17, 8192, 128) == 128             # 544: third round 32 of 256
+    assert ftr(1, 20, 8192, 128) == 128             # 640: third round half full
+    assert ftr(1, 21, 8192, 128) == 256             # 672
+    assert ftr(1, 25, 8192, 128) == 256             # 800: four rounds
     assert ftr(2, 16, 8192, 128) == 256             # 1024
     assert ftr(1, 1, 1, 128) == 128
-    # causal: at most one item per CU
+    # causal: at most one and a half items per CU
     assert ftr(1, 8, 8192, 128, causal=True) == 128   # 256
+    assert ftr(1, 12, 8192, 128, causal=True) == 128  # 384
+    assert ftr(1, 13, 8192, 128, causal=True) == 256  # 416
     assert ftr(1, 8, 16384, 128, causal=True) == 256  # 512
-    assert ftr(1, 12, 8192, 128, causal=True) == 256  # 384
     # packed: B does not multiply (the sequences share the token axis)
     assert ftr(8, 4, 8192, 128, packed=True) == 128
     assert ftr(8, 4, 8192, 128) == 256
@@ -99,10 +105,11 @@ def test_fwd_tile_rows_rule(lib):
     assert ftr(1, 4, 8192, 128, num_cus=-1) == 128
     # exhaustive against the stated rule on a grid of shapes
     for cus in (80, 256, 304):
-        for items in range(1, 3 * cus):
-            nc = 2 * items <= cus or (cus < items < 2 * cus and 2 * (items - cus) <= cus)
+        for items in range(1, 4 * cus):
+            last = items % cus
+            nc = 2 * items <= cus or (cus < items < 3 * cus and 0 < last and 2 * last <= cus)
             assert ftr(1, items, 256, 128, num_cus=cus) == (128 if nc else 256), (cus, items)
-            assert ftr(1, items, 200, 128, causal=True, num_cus=cus) == (128 if items <= cus else 256)
+            assert ftr(1, items, 200, 128, causal=True, num_cus=cus) == (128 if 2 * items <= 3 * cus else 256)
 
 
 # Fake but plausible device addresses: validation rejects before using them.

@@ -272,11 +272,13 @@ def test_four_wave_tiles_edges_and_packed(causal):
         assert torch.equal(o.view(torch.int16), o8.view(torch.int16)) and torch.equal(lse, l8)
 
 
-# (B, H, N, causal) at the edges of the rule: 256-row items = C/2, C, 1.5 C and
-# 2 C (+1) on a 256-CU MI355X
+# (B, H, N, causal) at the edges of the rule: 256-row items = C/2, C, 1.5 C,
+# 2 C, 2.5 C and 3 C (+1) on a 256-CU MI355X
 BOUNDARY_SHAPES = [(1, 128, 256, False), (1, 129, 256, False), (1, 256, 256, False), (1, 257, 256, False),
-                   (1, 384, 256, False), (1, 385, 200, False), (2, 128, 512, False), (1, 512, 129, False),
-                   (1, 256, 256, True), (1, 257, 256, True), (2, 64, 300, True)]
+                   (1, 384, 256, False), (1, 385, 200, False), (2, 128, 512, False), (1, 513, 129, False),
+                   (1, 640, 256, False), (1, 641, 256, False), (1, 769, 256, False),
+                   (1, 256, 256, True), (1, 257, 256, True), (1, 384, 256, True), (1, 385, 256, True),
+                   (2, 64, 300, True)]
 
 
 @pytest.mark.parametrize("shape", BOUNDARY_SHAPES, ids=lambda s: "B{}_H{}_N{}_{}".format(*s))
