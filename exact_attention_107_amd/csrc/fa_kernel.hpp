@@ -653,6 +653,24 @@ fa_fwd_kernel(Params p) {
         return (CAUSAL && kv0 + BC - 1 > wrow0) || kv0 + BC > n;
     };
     const float bias_coef = MODS && p.alibi ? p.alibi[w.h] * p.inv_scale : 0.0f;
+    // linear bias of block b: slope (j - i) on the scaled score = slope / scale
+    // on the raw one; j - i = (k0 - qrow) + C
+    auto s_bias_block = [&](f32x16 (&s)[QB][NKB], int b, int k0, int qrow) {
+        const float base = static_cast<float>(k0 - qrow);
+#pragma unroll
+        for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int C = kb2 * 32 + (r >> 2) * 8 + (r & 3);
+                s[b][kb2][r] = __builtin_fmaf(bias_coef, base + static_cast<float>(C), s[b][kb2][r]);
+            }
+    };
+    // the bias alone, for tiles that no window edge or tail cuts
+    auto s_bias = [&](f32x16 (&s)[QB][NKB], int j) {
+        const int k0 = (kt0 + j) * BC + 4 * hh;
+#pragma unroll
+        for (int b = 0; b < QB; ++b) s_bias_block(s, b, k0, wrow0 + 32 * b + c);
+    };
     auto s_mask = [&](f32x16 (&s)[QB][NKB], int j) {
         const int kv0 = (kt0 + j) * BC;
 #pragma unroll
@@ -681,18 +699,7 @@ fa_fwd_kernel(Params p) {
             if (CAUSAL) hi = min(hi, qrow - k0 + 1);
             if (p.wr >= 0) hi = min(hi, qrow + p.wr - k0 + 1);
             const int lo = p.wl >= 0 ? qrow - p.wl - k0 : -BC;
-            if (p.alibi != nullptr) {
-                // slope (j - i) on the scaled score = slope / scale on the raw one;
-                // j - i = (k0 - qrow) + C
-                const float base = static_cast<float>(k0 - qrow);
-#pragma unroll
-                for (int kb2 = 0; kb2 < NKB; ++kb2)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int C = kb2 * 32 + (r >> 2) * 8 + (r & 3);
-                        s[b][kb2][r] = __builtin_fmaf(bias_coef, base + static_cast<float>(C), s[b][kb2][r]);
-                    }
-            }
+            if (p.alibi != nullptr) s_bias_block(s, b, k0, qrow);
 #pragma unroll
             for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
@@ -990,7 +997,8 @@ fa_fwd_kernel(Params p) {
         phase_a(nxt, cur, (PAR ? k_lds0 : k_lds1), kf);  // K_{j+1}
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (decltype(mask)::value) s_mask(nxt, j + 1);
+        if constexpr (decltype(mask)::value == 1) s_mask(nxt, j + 1);
+        else if constexpr (decltype(mask)::value == 2) s_bias(nxt, j + 1);
         half_barrier();
         float mx[QB];
         phase_b(nxt, cur, (PAR ? v_lds1 : v_lds0), mx);  // V_j
@@ -1011,20 +1019,22 @@ fa_fwd_kernel(Params p) {
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    using NoMask = std::integral_constant<bool, false>;
-    using Mask = std::integral_constant<bool, true>;
+    // what a step does to its next tile's scores: nothing, the tail / causal /
+    // window mask (with the bias, if any), or the bias alone
+    using NoMask = std::integral_constant<int, 0>;
+    using Mask = std::integral_constant<int, 1>;
+    using BiasOnly = std::integral_constant<int, 2>;
 
     // first tile that needs a mask (tail: n / BC; causal: (wrow0 + 1) / BC)
     // (windows: the right edge plays the diagonal's part, the left edge masks
-    // the first tiles, jh of them rounded up to a pair; a bias needs every
-    // tile to go through the mask step)
+    // the first tiles, jh of them rounded up to a pair; a bias goes on every
+    // tile, with the mask or alone)
     int jm = (CAUSAL ? min(n / BC, (wrow0 + 1) / BC) : n / BC) - kt0;
     int jh = 0;
     if constexpr (MODS) {
         jm = (p.wr >= 0 ? min(n / BC, (wrow0 + p.wr + 1) / BC) : n / BC) - kt0;
         if (p.wl >= 0) jh = max(0, (wrow0 + RW - 1 - p.wl - kt0 * BC + BC) / BC);
         jh = (jh + 1) & ~1;
-        if (p.alibi) jm = -1;
     }
     const int lim = min(nkv_w, jm);
     int j = 0;
@@ -1035,7 +1045,16 @@ fa_fwd_kernel(Params p) {
         full_step(I0{}, Mask{}, sa, sb, j);
         full_step(I1{}, Mask{}, sb, sa, j + 1);
     }
-    // hot loop: pairs of full steps whose next tiles need no mask
+    // hot loop: pairs of full steps whose next tiles need no mask (with a
+    // bias: the bias alone)
+    if constexpr (MODS) {
+        if (p.alibi != nullptr) {
+            for (; j + 2 < lim; j += 2) {
+                full_step(I0{}, BiasOnly{}, sa, sb, j);
+                full_step(I1{}, BiasOnly{}, sb, sa, j + 1);
+            }
+        }
+    }
     for (; j + 2 < lim; j += 2) {
         full_step(I0{}, NoMask{}, sa, sb, j);
         full_step(I1{}, NoMask{}, sb, sa, j + 1);
