@@ -11,21 +11,30 @@ KernelFp8Fn select_fp8_d256(bool causal, bool packed) { return select_fp8<256>(c
 int launch_quant(const QuantParams &qp, void *stream) {
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const long long bh = static_cast<long long>(qp.B) * qp.H;
+    // token slices per (sequence, head) of the amax (and packed code) kernels:
+    // 256 tokens each (dense); packed, twice the average sequence's count
+    long long slices;
     if (qp.cu) {
-        // packed: one workgroup per (sequence, head) for both steps
-        if (bh > 0x7fffffffLL) return -1;
-        hipLaunchKernelGGL(fa_fp8_amax_packed_kernel, dim3(static_cast<unsigned>(bh)), dim3(256), 0, st, qp);
-        if (hipGetLastError() != hipSuccess) return -1;
-        hipLaunchKernelGGL(fa_fp8_quant_packed_kernel, dim3(static_cast<unsigned>(bh)), dim3(256), 0, st, qp);
-        return hipGetLastError() == hipSuccess ? 0 : -1;
+        const long long avg = (static_cast<long long>(qp.N) + 256LL * qp.B - 1) / (256LL * qp.B);
+        slices = avg * 2 < 1 ? 1 : (avg * 2 > 1024 ? 1024 : avg * 2);
+    } else {
+        slices = (static_cast<long long>(qp.N) + 255) / 256;
     }
+    const long long sgrid = bh * slices;
+    const long long bgrid = (bh + 255) / 256;
     const long long tokens = qp.transpose ? (qp.N + 63) / 64 * 64 : qp.N;
-    const long long items = bh * tokens * (qp.d / 4);
-    const long long grid = (items + 255) / 256;
-    if (bh > 0x7fffffffLL || grid > 0x7fffffffLL) return -1;
-    hipLaunchKernelGGL(fa_fp8_amax_kernel, dim3(static_cast<unsigned>(bh)), dim3(256), 0, st, qp);
+    const long long qgrid = qp.cu ? sgrid : (bh * tokens * (qp.d / 4) + 255) / 256;
+    if (sgrid > 0x7fffffffLL || qgrid > 0x7fffffffLL) return -1;
+    hipLaunchKernelGGL(fa_fp8_amax_init_kernel, dim3(static_cast<unsigned>(bgrid)), dim3(256), 0, st, qp);
     if (hipGetLastError() != hipSuccess) return -1;
-    hipLaunchKernelGGL(fa_fp8_quant_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, qp);
+    hipLaunchKernelGGL(fa_fp8_amax_kernel, dim3(static_cast<unsigned>(sgrid)), dim3(256), 0, st, qp);
+    if (hipGetLastError() != hipSuccess) return -1;
+    if (qp.cu)
+        hipLaunchKernelGGL(fa_fp8_quant_packed_kernel, dim3(static_cast<unsigned>(qgrid)), dim3(256), 0, st, qp);
+    else
+        hipLaunchKernelGGL(fa_fp8_quant_kernel, dim3(static_cast<unsigned>(qgrid)), dim3(256), 0, st, qp);
+    if (hipGetLastError() != hipSuccess) return -1;
+    hipLaunchKernelGGL(fa_fp8_descale_kernel, dim3(static_cast<unsigned>(bgrid)), dim3(256), 0, st, qp);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

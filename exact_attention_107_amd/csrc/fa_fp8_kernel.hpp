@@ -409,32 +409,80 @@ fa_fp8_fwd_kernel(Fp8Params p) {
 // ---------------------------------------------------------------------------
 // Quantisation: descale[bh] = amax / 448 (1 for an all-zero head), codes =
 // E4M3(x * (1 / descale)), every step in fp32 with IEEE rounding.
+//
+// Four launches on the stream.  Until the last one the descale array holds
+// each (sequence, head)'s running amax as a bit pattern: |x| >= 0, so the
+// integer order of the bits is the float order and an atomic maximum over
+// the workgroups of a head is exact whatever their order.  The array is
+// zeroed; each workgroup reduces one slice of the tokens of one (sequence,
+// head) and merges its maximum; the codes are written from the finished
+// amax; the amax is turned into the descale.  The amax and packed code
+// kernels run (sequence, head) x slices workgroups, slices = grid / (B H).
+
+__device__ __forceinline__ float fp8_descale_of(float amax) { return amax > 0.0f ? amax / 448.0f : 1.0f; }
+
+// tokens of sequence b: the first one on the token axis and the count
+__device__ __forceinline__ void fp8_quant_seq(const QuantParams &p, int b, long long &t0, int &n) {
+    if (p.cu) {
+        int a, e;
+        seq_span(p.cu, b, p.N, a, e);
+        t0 = a;
+        n = e - a;
+    } else {
+        t0 = static_cast<long long>(b) * p.N;
+        n = p.N;
+    }
+}
+
+// slice s of n tokens cut into `slices` near-equal parts: [lo, hi)
+__device__ __forceinline__ void fp8_quant_slice(int n, int s, int slices, int &lo, int &hi) {
+    const long long per = (static_cast<long long>(n) + slices - 1) / slices;
+    lo = static_cast<int>(min(static_cast<long long>(n), s * per));
+    hi = static_cast<int>(min(static_cast<long long>(n), lo + per));
+}
+
+__global__ void __launch_bounds__(256) fa_fp8_amax_init_kernel(QuantParams p) {
+    const long long i = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+    if (i < static_cast<long long>(p.B) * p.H) p.descale[i] = 0.0f;
+}
 
 __global__ void __launch_bounds__(256) fa_fp8_amax_kernel(QuantParams p) {
-    const int bh = blockIdx.x;
+    const int slices = static_cast<int>(gridDim.x / (static_cast<unsigned>(p.B) * p.H));
+    const int bh = blockIdx.x / slices, s = blockIdx.x - bh * slices;
     const int b = bh / p.H, h = bh - b * p.H;
-    const int chunks = p.d / 8;                        // 16-byte chunks per row
-    const long long total = static_cast<long long>(p.N) * chunks;
+    long long t0;
+    int n, lo, hi;
+    fp8_quant_seq(p, b, t0, n);
+    fp8_quant_slice(n, s, slices, lo, hi);
+    const int chunks = p.d / 8;  // 16-byte chunks per row
+    const long long total = static_cast<long long>(hi - lo) * chunks;
+    const uint16_t *xs = p.x + ((t0 + lo) * p.H + h) * p.d;
+    const long long rs = static_cast<long long>(p.H) * p.d;
     float m = 0.0f;
+#pragma unroll 4
     for (long long t = threadIdx.x; t < total; t += 256) {
         const long long i = t / chunks;
         const int cc = static_cast<int>(t - i * chunks);
-        const u32x4 w = *reinterpret_cast<const u32x4 *>(
-            p.x + ((static_cast<long long>(b) * p.N + i) * p.H + h) * p.d + cc * 8);
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(xs + i * rs + cc * 8);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             m = fmaxf(m, fabsf(__uint_as_float(w[k] << 16)));
             m = fmaxf(m, fabsf(__uint_as_float(w[k] & 0xffff0000u)));
         }
     }
-    __shared__ float red[256];
-    red[threadIdx.x] = m;
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    __shared__ float red[4];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if (threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
-        __syncthreads();
+    if (threadIdx.x == 0) {
+        m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        if (m > 0.0f) atomicMax(reinterpret_cast<unsigned int *>(p.descale) + bh, __float_as_uint(m));
     }
-    if (threadIdx.x == 0) p.descale[bh] = red[0] > 0.0f ? red[0] / 448.0f : 1.0f;
+}
+
+__global__ void __launch_bounds__(256) fa_fp8_descale_kernel(QuantParams p) {
+    const long long i = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+    if (i < static_cast<long long>(p.B) * p.H) p.descale[i] = fp8_descale_of(p.descale[i]);
 }
 
 // one thread per (token, 4 columns); transposed: 64 consecutive tokens of a
@@ -470,7 +518,7 @@ __global__ void __launch_bounds__(256) fa_fp8_quant_kernel(QuantParams p) {
         for (int k = 0; k < 4; ++k) row[static_cast<long long>(k) * np] = 0;
         return;
     }
-    const float inv = 1.0f / p.descale[bh];
+    const float inv = 1.0f / fp8_descale_of(p.descale[bh]);
     const u32x2 w = *reinterpret_cast<const u32x2 *>(
         p.x + ((static_cast<long long>(b) * p.N + i) * p.H + h) * p.d + cq * 4);
     const float x0 = __uint_as_float(w[0] << 16) * inv, x1 = __uint_as_float(w[0] & 0xffff0000u) * inv;
@@ -485,58 +533,31 @@ __global__ void __launch_bounds__(256) fa_fp8_quant_kernel(QuantParams p) {
     }
 }
 
-// Packed sequences: one workgroup per (sequence, head).  amax over the
-// sequence's tokens, then its codes: [T, H, d] in place of x, or the
-// sequence's columns of the packed V^T rows (zero codes up to the next
+// Packed sequences: the codes of one token slice of one (sequence, head):
+// [T, H, d] in place of x, or the slice's columns of the packed V^T rows
+// (the sequence's last slice also writes the zero codes up to the next
 // multiple of 64 keys; columns past the last sequence's padding are not
 // written).
-__global__ void __launch_bounds__(256) fa_fp8_amax_packed_kernel(QuantParams p) {
-    const int bh = blockIdx.x;
-    const int b = bh / p.H, h = bh - b * p.H;
-    int t0, t1;
-    seq_span(p.cu, b, p.N, t0, t1);
-    const int n = t1 - t0;
-    const int chunks = p.d / 8;
-    const long long total = static_cast<long long>(n) * chunks;
-    float m = 0.0f;
-    for (long long t = threadIdx.x; t < total; t += 256) {
-        const long long i = t / chunks;
-        const int cc = static_cast<int>(t - i * chunks);
-        const u32x4 w = *reinterpret_cast<const u32x4 *>(p.x + ((t0 + i) * p.H + h) * p.d + cc * 8);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            m = fmaxf(m, fabsf(__uint_as_float(w[k] << 16)));
-            m = fmaxf(m, fabsf(__uint_as_float(w[k] & 0xffff0000u)));
-        }
-    }
-    __shared__ float red[256];
-    red[threadIdx.x] = m;
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if (threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) p.descale[bh] = red[0] > 0.0f ? red[0] / 448.0f : 1.0f;
-}
-
 __global__ void __launch_bounds__(256) fa_fp8_quant_packed_kernel(QuantParams p) {
-    const int bh = blockIdx.x;
+    const int slices = static_cast<int>(gridDim.x / (static_cast<unsigned>(p.B) * p.H));
+    const int bh = blockIdx.x / slices, s = blockIdx.x - bh * slices;
     const int b = bh / p.H, h = bh - b * p.H;
-    int t0, t1;
-    seq_span(p.cu, b, p.N, t0, t1);
-    const int n = t1 - t0;
+    long long t0;
+    int n, lo, hi;
+    fp8_quant_seq(p, b, t0, n);
+    fp8_quant_slice(n, s, slices, lo, hi);
     const int q4 = p.d / 4;
-    const float inv = 1.0f / p.descale[bh];
+    const float inv = 1.0f / fp8_descale_of(p.descale[bh]);
     auto codes_of = [&](long long tok, int cq) {
         const u32x2 w = *reinterpret_cast<const u32x2 *>(p.x + (tok * p.H + h) * p.d + cq * 4);
         return pack_fp8x4(__uint_as_float(w[0] << 16) * inv, __uint_as_float(w[0] & 0xffff0000u) * inv,
                           __uint_as_float(w[1] << 16) * inv, __uint_as_float(w[1] & 0xffff0000u) * inv);
     };
     if (!p.transpose) {
-        const long long total = static_cast<long long>(n) * q4;
+        const long long total = static_cast<long long>(hi - lo) * q4;
         for (long long t = threadIdx.x; t < total; t += 256) {
-            const long long i = t / q4;
-            const int cq = static_cast<int>(t - i * q4);
+            const long long i = lo + t / q4;
+            const int cq = static_cast<int>(t % q4);
             *reinterpret_cast<int *>(p.x8 + ((t0 + i) * p.H + h) * p.d + cq * 4) = codes_of(t0 + i, cq);
         }
         return;
@@ -545,10 +566,12 @@ __global__ void __launch_bounds__(256) fa_fp8_quant_packed_kernel(QuantParams p)
     const int pad = (n + 63) / 64 * 64;
     const int start = fp8_packed_vt_start(p.cu, b, p.N, p.vts);
     if (start + pad > p.vts) return;   // malformed offsets only
-    const long long total = static_cast<long long>(pad) * q4;
+    const int end = s == slices - 1 ? pad : hi;
+    const int width = end - lo;
+    const long long total = static_cast<long long>(width) * q4;
     for (long long t = threadIdx.x; t < total; t += 256) {
-        const int cq = static_cast<int>(t / pad);
-        const int u = static_cast<int>(t - static_cast<long long>(cq) * pad);
+        const int cq = static_cast<int>(t / width);
+        const int u = lo + static_cast<int>(t - static_cast<long long>(cq) * width);
         const int codes = u < n ? codes_of(t0 + u, cq) : 0;
         uint8_t *row = p.x8 + (static_cast<long long>(h) * p.d + cq * 4) * p.vts + start + u;
 #pragma unroll
