@@ -401,8 +401,11 @@ int fa_fwd_fp8(const void *q8, const void *k8, const void *vt8,
  * that head (1 for an all-zero head) and codes = E4M3(x * (1 / descale)),
  * rounded to nearest even, every step in fp32.  transpose = 0 writes x8 as
  * [B, N, H, d]; transpose != 0 writes [B, H, d, fa_fp8_vt_stride(N)] with
- * zero codes in the padding (the V layout of fa_fwd_fp8).  Two kernels on
- * `stream`; errors as fa_fwd.
+ * zero codes in the padding (the V layout of fa_fwd_fp8).  Four kernels on
+ * `stream`: until the last one, descale holds each head's running amax (so
+ * it must not alias x or x8); the amax is reduced over 256-token slices and
+ * merged with an atomic maximum, which is exact, so the result does not
+ * depend on the order of the workgroups.  Errors as fa_fwd.
  */
 int fa_quantize_fp8(const void *x, void *x8, float *descale, int B, int H,
                     int N, int d, int transpose, hipStream_t stream);
@@ -435,9 +438,9 @@ int fa_fp8_vt_stride_packed(int T, int B);
  * writes x8 as [T, H, d]; transpose != 0 writes the packed V^T layout
  * [H, d, fa_fp8_vt_stride_packed(T, B)]: sequence b's codes and zero codes up
  * to its next multiple of 64 keys; the columns past the last sequence's
- * padding are not written.  One workgroup per (sequence, head) for each of
- * the two kernels on `stream`.  Errors as fa_quantize_fp8; FA_ERR_NULLPTR
- * for cu_seqlens == NULL.
+ * padding are not written.  The same four kernels on `stream`, each
+ * sequence's tokens cut into equal slices for the amax and the codes.
+ * Errors as fa_quantize_fp8; FA_ERR_NULLPTR for cu_seqlens == NULL.
  */
 int fa_quantize_fp8_packed(const void *x, void *x8, float *descale,
                            const int32_t *cu_seqlens, int B, int H, int T,
