@@ -403,6 +403,49 @@ def other_pass(torch, fa, which, workload, steps, warmup, settle_s=0.0):
     return res, f, ms_step, ms, label
 
 
+def reference_copy(torch, mib: int) -> None:
+    """One plain device copy of `mib` MiB: a dispatch of known bytes to scale
+    the HBM byte counters by."""
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def quant_pass(torch, fa, workload, steps, warmup, settle_s=0.0):
+    """The per-(sequence, head) E4M3 quantisation an FP8 forward needs, for
+    profiling: Q and K in their own layout and V transposed, one step = the
+    three calls."""
+    from exact_attention_107_amd.workloads import RUNS, make_inputs
+    r = RUNS[workload]
+    ri = make_inputs(r)
+    q, k, v = (to_dev(ri[x], torch) for x in ("q", "k", "v"))
+    cu = torch.from_numpy(ri["cu_seqlens"]).cuda() if ri["cu_seqlens"] is not None else None
+    if cu is None:
+        outs = [fa.quantize_fp8(x, transpose=t) for x, t in ((q, False), (k, False), (v, True))]
+    else:
+        outs = [fa.quantize_fp8_packed(x, cu, transpose=t) for x, t in ((q, False), (k, False), (v, True))]
+
+    def launch():
+        for (x, t), (c, d) in zip(((q, False), (k, False), (v, True)), outs):
+            if cu is None:
+                fa.quantize_fp8(x, transpose=t, out=c, descale=d)
+            else:
+                fa.quantize_fp8_packed(x, cu, transpose=t, out=c, descale=d)
+    label = f"{r.name}: B={r.B} H={r.H} N={ri['N']} d={r.d}{' packed' if cu is not None else ''}, Q and K " \
+            "in their layout, V transposed"
+    log(f"[bench] quant pass on {label}")
+    res = {}
+    if settle_s > 0:
+        res["clock_settle_launches"] = settle_clock(launch, settle_s, torch)
+    ms_step, ms, _, _ = time_launches(launch, steps, warmup, torch)
+    nbytes = 3 * q.numel() * 2
+    res.update({"ms": round(ms, 5), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes_bf16_per_step": nbytes})
+    return res, ms_step, label
+
+
 def rescale_rates(torch, fa):
     """How often the conditional rescale fires (counting instance of the
     kernel, one launch per run and rule): the share of wave-steps (64 keys x 32
@@ -463,12 +506,13 @@ def main() -> int:
     ap.add_argument("--extra", type=int, default=1, help="also time the other runs and variants")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "fp8", "split", "masked", "pingpong"),
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "fp8", "split", "masked", "pingpong", "quant"),
                     default="fwd",
                     help="time only one other kernel family on --workload (for profiling): bwd = the "
                          "backward pass, fp8 = the FP8 forward, split = the split-KV forward and merge, "
                          "masked = the 1024-key sliding window with ALiBi (fixed shape), pingpong = the "
-                         "two-query-tile ping-pong schedule of the forward (d = 128, dense)")
+                         "two-query-tile ping-pong schedule of the forward (d = 128, dense), quant = the "
+                         "FP8 quantisation of Q, K and V^T")
     ap.add_argument("--settle-s", type=float, default=0.5,
                     help="seconds of untimed launches before the warmup, so that the timed steps "
                          "run at the clock the GPU holds under this load (0: none)")
@@ -501,6 +545,17 @@ def main() -> int:
             "config": {"workload": f"{args.workload}: {res['shape']}"}, "roofline": res["roofline"],
             "kernel_fingerprint": kernel_fingerprint()}), flush=True)
         return 0
+    if args.which == "quant":
+        if args.copy_mb:
+            reference_copy(torch, args.copy_mb)
+        res, ms_step, label = quant_pass(torch, fa, args.workload, args.steps, args.warmup, args.settle_s)
+        print(json.dumps({
+            "metric": "FP8 quantisation of Q, K, V^T, GB/s (bf16 bytes of the three inputs per step)",
+            "value": res["gbs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "fp8-e4m3", "data": "synthetic", "config": {"workload": label}, "result": res,
+            "kernel_fingerprint": kernel_fingerprint()}), flush=True)
+        return 0
     if args.which in ("fp8", "split", "masked", "pingpong"):
         res, f, ms_step, ms_kernel, label = other_pass(torch, fa, args.which, args.workload, args.steps,
                                                        args.warmup, args.settle_s)
@@ -527,12 +582,7 @@ def main() -> int:
         fa.fwd(q, k, v, causal=inp["causal"], scale=inp["scale"], cu_seqlens=cu, out=o, lse=lse)
 
     if args.copy_mb:
-        src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        reference_copy(torch, args.copy_mb)
     settle_launches = settle_clock(launch, args.settle_s, torch) if args.settle_s > 0 else 0
     log(f"[bench] timing {args.steps} steps after {args.warmup} warmup "
         f"({settle_launches} launches to settle the clock first)")

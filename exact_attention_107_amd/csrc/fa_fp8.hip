@@ -22,8 +22,9 @@ int launch_quant(const QuantParams &qp, void *stream) {
     }
     const long long sgrid = bh * slices;
     const long long bgrid = (bh + 255) / 256;
-    const long long tokens = qp.transpose ? (qp.N + 63) / 64 * 64 : qp.N;
-    const long long qgrid = qp.cu ? sgrid : (bh * tokens * (qp.d / 4) + 255) / 256;
+    const long long qgrid = qp.cu ? sgrid
+                            : qp.transpose ? bh * ((qp.N + 63) / 64)        // 64-key tiles
+                                           : (bh * qp.N * (qp.d / 8) + 255) / 256;
     if (sgrid > 0x7fffffffLL || qgrid > 0x7fffffffLL) return -1;
     hipLaunchKernelGGL(fa_fp8_amax_init_kernel, dim3(static_cast<unsigned>(bgrid)), dim3(256), 0, st, qp);
     if (hipGetLastError() != hipSuccess) return -1;
@@ -31,6 +32,8 @@ int launch_quant(const QuantParams &qp, void *stream) {
     if (hipGetLastError() != hipSuccess) return -1;
     if (qp.cu)
         hipLaunchKernelGGL(fa_fp8_quant_packed_kernel, dim3(static_cast<unsigned>(qgrid)), dim3(256), 0, st, qp);
+    else if (qp.transpose)
+        hipLaunchKernelGGL(fa_fp8_quant_t_kernel, dim3(static_cast<unsigned>(qgrid)), dim3(256), 0, st, qp);
     else
         hipLaunchKernelGGL(fa_fp8_quant_kernel, dim3(static_cast<unsigned>(qgrid)), dim3(256), 0, st, qp);
     if (hipGetLastError() != hipSuccess) return -1;

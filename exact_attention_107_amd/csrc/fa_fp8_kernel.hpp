@@ -485,98 +485,131 @@ __global__ void __launch_bounds__(256) fa_fp8_descale_kernel(QuantParams p) {
     if (i < static_cast<long long>(p.B) * p.H) p.descale[i] = fp8_descale_of(p.descale[i]);
 }
 
-// one thread per (token, 4 columns); transposed: 64 consecutive tokens of a
-// column are written by the 64 lanes of a wave (one 64-byte row segment),
-// rows padded with zero codes to np = ceil(N/64)*64 tokens
+// 8 codes of 8 consecutive bf16 values (one 16-byte read; two 4-byte writes,
+// the codes being only 4-byte aligned)
+__device__ __forceinline__ void fp8_quant8(const uint16_t *src, uint8_t *dst, float inv) {
+    const u32x4 w = *reinterpret_cast<const u32x4 *>(src);
+    uint32_t out[2];
+    out[0] = static_cast<uint32_t>(
+        pack_fp8x4(__uint_as_float(w[0] << 16) * inv, __uint_as_float(w[0] & 0xffff0000u) * inv,
+                   __uint_as_float(w[1] << 16) * inv, __uint_as_float(w[1] & 0xffff0000u) * inv));
+    out[1] = static_cast<uint32_t>(
+        pack_fp8x4(__uint_as_float(w[2] << 16) * inv, __uint_as_float(w[2] & 0xffff0000u) * inv,
+                   __uint_as_float(w[3] << 16) * inv, __uint_as_float(w[3] & 0xffff0000u) * inv));
+    reinterpret_cast<uint32_t *>(dst)[0] = out[0];
+    reinterpret_cast<uint32_t *>(dst)[1] = out[1];
+}
+
+// codes in x's layout, one thread per (token, head, 8 columns)
 __global__ void __launch_bounds__(256) fa_fp8_quant_kernel(QuantParams p) {
     const long long t = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
-    const int q4 = p.d / 4;
-    const int np = (p.N + 63) / 64 * 64;
-    long long i, bh;
-    int cq;
-    if (p.transpose) {
-        // t = ((bh * q4 + cq) * np + i): lanes run along tokens
-        const long long per = static_cast<long long>(np);
-        i = t % per;
-        const long long r = t / per;
-        cq = static_cast<int>(r % q4);
-        bh = r / q4;
-    } else {
-        // t = ((b * N + i) * H + h) * q4 + cq: lanes run along columns
-        cq = static_cast<int>(t % q4);
-        const long long r = t / q4;
-        const int h = static_cast<int>(r % p.H);
-        const long long bi = r / p.H;
-        i = bi % p.N;
-        bh = (bi / p.N) * p.H + h;
-    }
+    const int g8 = p.d / 8;
+    // t = ((b * N + i) * H + h) * g8 + q: lanes run along columns
+    const int q = static_cast<int>(t % g8);
+    const long long r = t / g8;
+    const int h = static_cast<int>(r % p.H);
+    const long long bh = (r / p.H / p.N) * p.H + h;
     if (bh >= static_cast<long long>(p.B) * p.H) return;
+    fp8_quant8(p.x + r * p.d + q * 8, p.x8 + r * p.d + q * 8, 1.0f / fp8_descale_of(p.descale[bh]));
+}
+
+// Transposed codes of one 64-key tile of one (sequence, head), through LDS.
+// A thread takes four consecutive keys of 8 columns (16-byte reads, the
+// lanes of a column group reading whole rows), packs each column's four
+// codes into one dword of `tile` (column-major, rows padded to kTRow bytes so
+// that the column groups of a wave fall in different banks), and each of the
+// d V^T rows then receives one 64-byte run.  xs: the tile's first token,
+// head h; keys: its tokens present (the rest of the 64 are zero padding
+// codes); dst: V^T row 0 at the tile's first key; stride: V^T row length.
+constexpr int kTRow = 68;
+
+__device__ __forceinline__ void fp8_quant_t_tile(const QuantParams &p, float inv, const uint16_t *xs, int keys,
+                                                 uint8_t *dst, long long stride, uint8_t *tile) {
+    const int g8 = p.d / 8;
+    const long long rs = static_cast<long long>(p.H) * p.d;
+    for (int c = threadIdx.x; c < 16 * g8; c += 256) {
+        const int q = c % g8, rg = c / g8;
+        uint32_t col[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+            const int r = 4 * rg + k4;
+            if (r < keys) {
+                const u32x4 w = *reinterpret_cast<const u32x4 *>(xs + r * rs + q * 8);
+                const uint32_t lo = static_cast<uint32_t>(
+                    pack_fp8x4(__uint_as_float(w[0] << 16) * inv, __uint_as_float(w[0] & 0xffff0000u) * inv,
+                               __uint_as_float(w[1] << 16) * inv, __uint_as_float(w[1] & 0xffff0000u) * inv));
+                const uint32_t hi = static_cast<uint32_t>(
+                    pack_fp8x4(__uint_as_float(w[2] << 16) * inv, __uint_as_float(w[2] & 0xffff0000u) * inv,
+                               __uint_as_float(w[3] << 16) * inv, __uint_as_float(w[3] & 0xffff0000u) * inv));
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    col[k] |= ((lo >> (8 * k)) & 0xffu) << (8 * k4);
+                    col[4 + k] |= ((hi >> (8 * k)) & 0xffu) << (8 * k4);
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) *reinterpret_cast<uint32_t *>(tile + (q * 8 + j) * kTRow + 4 * rg) = col[j];
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < p.d * 16; c += 256) {
+        const int cl = c >> 4, part = c & 15;
+        *reinterpret_cast<uint32_t *>(dst + cl * stride + part * 4) =
+            *reinterpret_cast<const uint32_t *>(tile + cl * kTRow + part * 4);
+    }
+    __syncthreads();  // before the next tile overwrites `tile`
+}
+
+// transposed codes [B, H, d, np], np = ceil(N / 64) * 64: one workgroup per
+// 64-key tile of one (b, h)
+__global__ void __launch_bounds__(256) fa_fp8_quant_t_kernel(QuantParams p) {
+    __shared__ __attribute__((aligned(16))) uint8_t tile[256 * kTRow];
+    const int np = (p.N + 63) / 64 * 64;
+    const int tiles = np / 64;
+    const long long bh = blockIdx.x / tiles;
+    const int t = static_cast<int>(blockIdx.x - bh * tiles);
     const int b = static_cast<int>(bh / p.H), h = static_cast<int>(bh % p.H);
-    if (i >= p.N) {  // transposed padding
-        uint8_t *row = p.x8 + (bh * p.d + cq * 4) * np + i;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) row[static_cast<long long>(k) * np] = 0;
-        return;
-    }
     const float inv = 1.0f / fp8_descale_of(p.descale[bh]);
-    const u32x2 w = *reinterpret_cast<const u32x2 *>(
-        p.x + ((static_cast<long long>(b) * p.N + i) * p.H + h) * p.d + cq * 4);
-    const float x0 = __uint_as_float(w[0] << 16) * inv, x1 = __uint_as_float(w[0] & 0xffff0000u) * inv;
-    const float x2 = __uint_as_float(w[1] << 16) * inv, x3 = __uint_as_float(w[1] & 0xffff0000u) * inv;
-    const int codes = pack_fp8x4(x0, x1, x2, x3);
-    if (p.transpose) {
-        uint8_t *row = p.x8 + (bh * p.d + cq * 4) * np + i;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) row[static_cast<long long>(k) * np] = static_cast<uint8_t>(codes >> (8 * k));
-    } else {
-        *reinterpret_cast<int *>(p.x8 + ((static_cast<long long>(b) * p.N + i) * p.H + h) * p.d + cq * 4) = codes;
-    }
+    const int k0 = t * 64;
+    fp8_quant_t_tile(p, inv, p.x + ((static_cast<long long>(b) * p.N + k0) * p.H + h) * p.d, min(64, p.N - k0),
+                     p.x8 + bh * p.d * np + k0, np, tile);
 }
 
 // Packed sequences: the codes of one token slice of one (sequence, head):
-// [T, H, d] in place of x, or the slice's columns of the packed V^T rows
-// (the sequence's last slice also writes the zero codes up to the next
+// [T, H, d] in place of x, or the slice's 64-key tiles of the packed V^T
+// rows (the sequence's last tile carries the zero codes up to the next
 // multiple of 64 keys; columns past the last sequence's padding are not
 // written).
 __global__ void __launch_bounds__(256) fa_fp8_quant_packed_kernel(QuantParams p) {
+    __shared__ __attribute__((aligned(16))) uint8_t tile[256 * kTRow];
     const int slices = static_cast<int>(gridDim.x / (static_cast<unsigned>(p.B) * p.H));
     const int bh = blockIdx.x / slices, s = blockIdx.x - bh * slices;
     const int b = bh / p.H, h = bh - b * p.H;
     long long t0;
-    int n, lo, hi;
+    int n;
     fp8_quant_seq(p, b, t0, n);
-    fp8_quant_slice(n, s, slices, lo, hi);
-    const int q4 = p.d / 4;
     const float inv = 1.0f / fp8_descale_of(p.descale[bh]);
-    auto codes_of = [&](long long tok, int cq) {
-        const u32x2 w = *reinterpret_cast<const u32x2 *>(p.x + (tok * p.H + h) * p.d + cq * 4);
-        return pack_fp8x4(__uint_as_float(w[0] << 16) * inv, __uint_as_float(w[0] & 0xffff0000u) * inv,
-                          __uint_as_float(w[1] << 16) * inv, __uint_as_float(w[1] & 0xffff0000u) * inv);
-    };
     if (!p.transpose) {
-        const long long total = static_cast<long long>(hi - lo) * q4;
+        int lo, hi;
+        fp8_quant_slice(n, s, slices, lo, hi);
+        const int g8 = p.d / 8;
+        const long long total = static_cast<long long>(hi - lo) * g8;
         for (long long t = threadIdx.x; t < total; t += 256) {
-            const long long i = lo + t / q4;
-            const int cq = static_cast<int>(t % q4);
-            *reinterpret_cast<int *>(p.x8 + ((t0 + i) * p.H + h) * p.d + cq * 4) = codes_of(t0 + i, cq);
+            const long long r = (t0 + lo + t / g8) * p.H + h;
+            const int q = static_cast<int>(t % g8);
+            fp8_quant8(p.x + r * p.d + q * 8, p.x8 + r * p.d + q * 8, inv);
         }
         return;
     }
-    // transposed: lanes run along the sequence's (padded) keys
+    // transposed: the slice's share of the sequence's 64-key tiles
     const int pad = (n + 63) / 64 * 64;
     const int start = fp8_packed_vt_start(p.cu, b, p.N, p.vts);
     if (start + pad > p.vts) return;   // malformed offsets only
-    const int end = s == slices - 1 ? pad : hi;
-    const int width = end - lo;
-    const long long total = static_cast<long long>(width) * q4;
-    for (long long t = threadIdx.x; t < total; t += 256) {
-        const int cq = static_cast<int>(t / width);
-        const int u = lo + static_cast<int>(t - static_cast<long long>(cq) * width);
-        const int codes = u < n ? codes_of(t0 + u, cq) : 0;
-        uint8_t *row = p.x8 + (static_cast<long long>(h) * p.d + cq * 4) * p.vts + start + u;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) row[static_cast<long long>(k) * p.vts] = static_cast<uint8_t>(codes >> (8 * k));
-    }
+    int lo, hi;
+    fp8_quant_slice(pad / 64, s, slices, lo, hi);
+    for (int t = lo; t < hi; ++t)
+        fp8_quant_t_tile(p, inv, p.x + ((t0 + t * 64) * p.H + h) * p.d, min(64, n - t * 64),
+                         p.x8 + static_cast<long long>(h) * p.d * p.vts + start + t * 64, p.vts, tile);
 }
 
 template <int D>
