@@ -454,16 +454,15 @@ __global__ void __launch_bounds__(256) fa_fp8_amax_kernel(QuantParams p) {
     int n, lo, hi;
     fp8_quant_seq(p, b, t0, n);
     fp8_quant_slice(n, s, slices, lo, hi);
-    const int chunks = p.d / 8;  // 16-byte chunks per row
-    const long long total = static_cast<long long>(hi - lo) * chunks;
-    const uint16_t *xs = p.x + ((t0 + lo) * p.H + h) * p.d;
+    // each thread keeps one 16-byte column chunk and steps over the rows
+    const int chunks = p.d / 8;
+    const int step = 256 / chunks;
     const long long rs = static_cast<long long>(p.H) * p.d;
+    const uint16_t *xs = p.x + ((t0 + lo) * p.H + h) * p.d + (threadIdx.x % chunks) * 8;
     float m = 0.0f;
 #pragma unroll 4
-    for (long long t = threadIdx.x; t < total; t += 256) {
-        const long long i = t / chunks;
-        const int cc = static_cast<int>(t - i * chunks);
-        const u32x4 w = *reinterpret_cast<const u32x4 *>(xs + i * rs + cc * 8);
+    for (int i = threadIdx.x / chunks; i < hi - lo; i += step) {
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(xs + i * rs);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             m = fmaxf(m, fabsf(__uint_as_float(w[k] << 16)));
@@ -593,12 +592,10 @@ __global__ void __launch_bounds__(256) fa_fp8_quant_packed_kernel(QuantParams p)
         int lo, hi;
         fp8_quant_slice(n, s, slices, lo, hi);
         const int g8 = p.d / 8;
-        const long long total = static_cast<long long>(hi - lo) * g8;
-        for (long long t = threadIdx.x; t < total; t += 256) {
-            const long long r = (t0 + lo + t / g8) * p.H + h;
-            const int q = static_cast<int>(t % g8);
-            fp8_quant8(p.x + r * p.d + q * 8, p.x8 + r * p.d + q * 8, inv);
-        }
+        const long long off = ((t0 + lo) * p.H + h) * p.d + (threadIdx.x % g8) * 8;
+        const long long rs = static_cast<long long>(p.H) * p.d;
+        for (int i = threadIdx.x / g8; i < hi - lo; i += 256 / g8)
+            fp8_quant8(p.x + off + i * rs, p.x8 + off + i * rs, inv);
         return;
     }
     // transposed: the slice's share of the sequence's 64-key tiles
