@@ -351,8 +351,8 @@ int fa_fwd_rescale_counts(const void *q, const void *k, const void *v, void *o,
  *                  the scaled score (ALiBi).
  * Every other argument as fa_fwd (no cu_seqlens, no causal flag); N is at
  * most 2^30 (FA_ERR_SHAPE beyond).  Uses hardware exp and the threshold
- * rescale; tiles that a window edge cuts, the sequence tail, and every tile
- * when a bias is given go through the mask step.
+ * rescale; tiles that a window edge cuts and the sequence tail go through the
+ * mask step, and with a bias every other tile adds the bias alone.
  */
 int fa_fwd_masked(const void *q, const void *k, const void *v, void *o,
                   float *lse, int B, int H, int N, int d, float scale,
